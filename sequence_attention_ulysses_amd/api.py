@@ -1,0 +1,381 @@
+"""Python binding of the Ulysses C ABI (``include/uly.h``).
+
+Argument marshalling only: torch tensors are turned into pointers, strides
+and stream handles, and every step of the exchange runs in ``libuly.so``'s
+gfx950 kernels.  torch supplies device memory (target storage) and streams.
+
+Operands are rank-major 5-D tensors ``[P, B, S, H, D]`` whose first axis is
+the emulated rank; any strides are accepted as long as the head dimension is
+contiguous (so a fused QKV projection ``[P, B, S_l, 3, H, D]`` is passed as
+its views ``qkv[:, :, :, c]``).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import warnings
+
+import torch
+
+from . import _lib
+from ._lib import check
+
+_DTYPES = {torch.float16: _lib.F16, torch.bfloat16: _lib.BF16}
+_TORCH_DTYPES = {v: k for k, v in _DTYPES.items()}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError("only float16 and bfloat16 tensors are supported, got %s" % t.dtype) from None
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def describe(t: torch.Tensor) -> _lib.UlyTensor:
+    """uly_tensor of a rank-major [P, B, S, H, D] tensor (no copy)."""
+    if t.dim() != 5:
+        raise ValueError("operand must be 5-D [P, B, S, H, D], got shape %s" % (tuple(t.shape),))
+    d = _lib.UlyTensor()
+    d.data = t.data_ptr() if t.numel() else 0
+    d.dtype = _dtype_code(t)
+    d.reserved = 0
+    d.rank_stride = t.stride(0)
+    for i in range(4):
+        d.shape[i] = t.shape[1 + i]
+        d.stride[i] = t.stride(1 + i)
+    return d
+
+
+def rope_table_1d(rows: int, D: int, theta: float = 1e4, real_rows: int | None = None):
+    """Host fp32 cos/sin tables [rows, D/2] of the 1-D rotary (built by the library)."""
+    real_rows = rows if real_rows is None else real_rows
+    cos = torch.empty((rows, D // 2), dtype=torch.float32)
+    sin = torch.empty((rows, D // 2), dtype=torch.float32)
+    check(_lib.load().uly_rope_table_1d(cos.data_ptr(), sin.data_ptr(), rows, real_rows, D, float(theta)),
+          "uly_rope_table_1d")
+    return cos, sin
+
+
+def rope_table_3d(rows: int, D: int, grid_h: int, grid_w: int, pairs=(22, 21, 21), theta: float = 1e4,
+                  real_rows: int | None = None):
+    """Host fp32 cos/sin tables [rows, D/2] of the 3-D (t, h, w) rotary of a row-major latent grid."""
+    real_rows = rows if real_rows is None else real_rows
+    cos = torch.empty((rows, D // 2), dtype=torch.float32)
+    sin = torch.empty((rows, D // 2), dtype=torch.float32)
+    check(_lib.load().uly_rope_table_3d(cos.data_ptr(), sin.data_ptr(), rows, real_rows, D, grid_h, grid_w,
+                                         pairs[0], pairs[1], pairs[2], float(theta)), "uly_rope_table_3d")
+    return cos, sin
+
+
+def height_split(Hh: int, P: int):
+    """Heights of the P height shards (the first Hh % P ranks take one more row) and hmax."""
+    base, extra = divmod(Hh, P)
+    return [base + (1 if r < extra else 0) for r in range(P)], -(-Hh // P)
+
+
+class UlyssesContext:
+    """One Ulysses group of ``world_size`` emulated ranks on one GPU.
+
+    Owns the library context (comm stream, events, tagged target cache).
+    Targets are allocated by torch on first use of a key and registered with
+    the library, so steady-state steps allocate nothing.
+    """
+
+    def __init__(self, world_size: int, device: int | None = 0, max_targets: int = 12):
+        self._lib = _lib.load()
+        self.world_size = int(world_size)
+        self.device = device
+        self._handle = ctypes.c_void_p()
+        dev = -1 if device is None else int(device)
+        check(self._lib.uly_create(ctypes.byref(self._handle), dev, self.world_size, int(max_targets)),
+              "uly_create")
+        self._targets: dict[tuple, torch.Tensor] = {}
+        self._closed = False
+
+    # -- lifetime -----------------------------------------------------------
+    def close(self) -> None:
+        if not self._closed:
+            self._closed = True
+            st = self._lib.uly_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+            self._targets.clear()
+            check(st, "uly_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        # Warn only; teardown from a finalizer could race the caller's streams.
+        if not getattr(self, "_closed", True):
+            warnings.warn("UlyssesContext was not closed; call close()", ResourceWarning, stacklevel=2)
+
+    def _h(self):
+        if self._closed:
+            raise RuntimeError("UlyssesContext is closed")
+        return self._handle
+
+    def _on_device(self, *tensors) -> None:
+        """Every tensor handed to the library must live on this context's GPU."""
+        for t in tensors:
+            if t is None:
+                continue
+            if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.device.index != self.device:
+                raise ValueError("tensor must be on cuda:%s, got %s" % (self.device, getattr(t, "device", type(t))))
+
+    @staticmethod
+    def _check_out(out: torch.Tensor, like_dtype, numel: int, what: str) -> None:
+        """An explicit destination must be contiguous, of the operand dtype and large enough."""
+        if out.dtype != like_dtype or not out.is_contiguous() or out.numel() < numel:
+            raise ValueError("%s: destination must be a contiguous %s tensor of >= %d elements, got %s %s"
+                             % (what, like_dtype, numel, out.dtype, tuple(out.shape)))
+
+    # -- targets ------------------------------------------------------------
+    def target(self, tag: str, mode: int, dtype: torch.dtype, shape) -> torch.Tensor:
+        """The cached target of (tag, mode, dtype, per-rank shape); allocated once.
+
+        Returns a [P, *shape] view of the registered storage.  When the cache
+        is full the returned tensor is a one-shot buffer (not cached).
+        """
+        shape = tuple(int(s) for s in shape)
+        key = (tag, mode, dtype, shape)
+        t = self._targets.get(key)
+        if t is not None:
+            return t
+        numel = self.world_size * math.prod(shape)
+        buf = torch.empty(numel, dtype=dtype, device=torch.device("cuda", self.device))
+        st = self._lib.uly_target_register(self._h(), tag.encode(), mode, _DTYPES[dtype],
+                                           _lib.int64_array(shape), buf.data_ptr(), numel * 2)
+        view = buf.view((self.world_size,) + shape)
+        if st == _lib.E_CACHE_FULL:
+            warnings.warn("Ulysses target cache is full; '%s' uses a one-shot buffer" % tag, RuntimeWarning,
+                          stacklevel=3)
+            return view
+        check(st, "uly_target_register")
+        self._targets[key] = view
+        return view
+
+    def _dest(self, tag, mode, like: torch.Tensor, shape, out):
+        if out is not None:
+            self._on_device(out)
+            self._check_out(out, like.dtype, self.world_size * math.prod(shape), tag or "out")
+            return out, True
+        t = self.target(tag, mode, like.dtype, shape)
+        return t, (tag, mode, like.dtype, tuple(shape)) not in self._targets
+
+    # -- the exchange -----------------------------------------------------------
+    def scatter_qkv(self, q=None, k=None, v=None, tags=("q", "k", "v"), out=None, stream=None):
+        """Sequence-sharded -> head-sharded for up to three operands, one launch on the comm stream.
+
+        Returns the destination tensors [P, B, P*S_l, H/P, D] (None for absent members).
+        Pair with :meth:`wait` before consuming them.
+        """
+        P = self.world_size
+        mem = (q, k, v)
+        self._on_device(*mem)
+        descs, dests, ptrs = [], [], []
+        for i, x in enumerate(mem):
+            if x is None:
+                descs.append(None); dests.append(None); ptrs.append(None)
+                continue
+            if x.dim() != 5 or x.shape[3] % P:
+                # the library raises the precise error; shape here only sizes the target
+                descs.append(describe(x)); dests.append(None); ptrs.append(None)
+                continue
+            shape = (x.shape[1], x.shape[2] * P, x.shape[3] // P, x.shape[4])
+            d, explicit = self._dest(tags[i], _lib.MODE_SCATTER, x, shape, None if out is None else out[i])
+            descs.append(describe(x)); dests.append(d)
+            ptrs.append(d.data_ptr() if explicit else None)
+        args = [ctypes.byref(dd) if dd is not None else None for dd in descs]
+        check(self._lib.ulysses_scatter_qkv(self._h(), *args, _lib.tags_array(tags), _lib.ptr_array(ptrs),
+                                            _stream_handle(stream)), "ulysses_scatter_qkv")
+        return dests
+
+    def fused_qk_norm_rope_scatter(self, q, k, w_q, w_k, cos, sin, eps: float = 1e-6, tags=("q", "k"),
+                                   out=None, stream=None):
+        """Q/K RMSNorm + interleaved RoPE + scatter in one kernel on the caller's stream.
+
+        cos/sin: device fp32 [rows >= P*S_l, D/2] tables indexed by global position.
+        Returns the destination tensors [P, B, P*S_l, H/P, D] (None for an absent member).
+        """
+        P = self.world_size
+        mem = (q, k)
+        self._on_device(q, k, w_q, w_k, cos, sin)
+        descs, dests, ptrs = [], [], []
+        for i, x in enumerate(mem):
+            if x is None:
+                descs.append(None); dests.append(None); ptrs.append(None)
+                continue
+            if x.dim() != 5 or x.shape[3] % P:
+                descs.append(describe(x)); dests.append(None); ptrs.append(None)
+                continue
+            shape = (x.shape[1], x.shape[2] * P, x.shape[3] // P, x.shape[4])
+            d, explicit = self._dest(tags[i], _lib.MODE_SCATTER, x, shape, None if out is None else out[i])
+            descs.append(describe(x)); dests.append(d)
+            ptrs.append(d.data_ptr() if explicit else None)
+        for t in (cos, sin):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2:
+                raise ValueError("cos/sin tables must be contiguous fp32 [rows, D/2]")
+        if cos.shape != sin.shape:
+            raise ValueError("cos and sin tables differ in shape")
+        args = [ctypes.byref(dd) if dd is not None else None for dd in descs]
+        wq = w_q.data_ptr() if (w_q is not None and q is not None) else None
+        wk = w_k.data_ptr() if (w_k is not None and k is not None) else None
+        for w, x in ((w_q, q), (w_k, k)):
+            if x is not None and w is not None and (w.dtype != x.dtype or not w.is_contiguous()
+                                                    or w.numel() != x.shape[-1]):
+                raise ValueError("norm weights must be contiguous [D] tensors in the operand dtype")
+        for x in (q, k):
+            if x is not None and x.dim() == 5 and cos.shape[1] * 2 != x.shape[-1]:
+                raise ValueError("cos/sin tables must have D/2 columns")
+        check(self._lib.fused_qk_norm_rope_scatter(self._h(), *args, wq, wk, float(eps), cos.data_ptr(),
+                                                   sin.data_ptr(), cos.shape[0], _lib.tags_array(tags),
+                                                   _lib.ptr_array(ptrs), _stream_handle(stream)),
+              "fused_qk_norm_rope_scatter")
+        return dests
+
+    def wait(self, stream=None) -> None:
+        """Grouped handshake: ``stream`` (default: current) waits for all scatters since the last wait."""
+        check(self._lib.uly_wait(self._h(), _stream_handle(stream)), "uly_wait")
+
+    def gather_out(self, o, tag: str = "out", out=None, stream=None) -> torch.Tensor:
+        """Head-sharded [P, B, S, Hl, D] -> sequence-sharded [P, B, S/P, P*Hl, D] on the caller's stream."""
+        P = self.world_size
+        self._on_device(o, out)
+        if o.dim() != 5:
+            raise ValueError("operand must be 5-D [P, B, S, Hl, D]")
+        if out is not None:
+            self._check_out(out, o.dtype, o.numel(), "gather_out")
+        shape = (o.shape[1], o.shape[2] // P, o.shape[3] * P, o.shape[4])
+        if out is None and o.shape[2] % P == 0:
+            dest = self.target(tag, _lib.MODE_GATHER, o.dtype, shape)
+            explicit = (tag, _lib.MODE_GATHER, o.dtype, shape) not in self._targets
+        else:
+            dest, explicit = out, out is not None
+        check(self._lib.ulysses_gather_out(self._h(), ctypes.byref(describe(o)), tag.encode() if tag else None,
+                                           dest.data_ptr() if explicit and dest is not None else None,
+                                           _stream_handle(stream)), "ulysses_gather_out")
+        return dest
+
+    # -- sequence padding ---------------------------------------------------------
+    def seq_pad_shard(self, full: torch.Tensor, S_l: int, out=None, stream=None) -> torch.Tensor:
+        """full [B, S, *row] -> rank-major [P, B, S_l, *row], zero rows past S."""
+        self._on_device(full, out)
+        B, S = full.shape[:2]
+        row = tuple(full.shape[2:])
+        if not full.is_contiguous():
+            raise ValueError("full must be contiguous")
+        if out is None:
+            out = torch.empty((self.world_size, B, S_l) + row, dtype=full.dtype, device=full.device)
+        self._check_out(out, full.dtype, self.world_size * B * S_l * math.prod(row), "seq_pad_shard")
+        check(self._lib.uly_seq_pad_shard(self._h(), full.data_ptr(), _dtype_code(full), B, S,
+                                          math.prod(row), S_l, out.data_ptr(), _stream_handle(stream)),
+              "uly_seq_pad_shard")
+        return out
+
+    def seq_unshard_trim(self, x: torch.Tensor, S: int, out=None, stream=None) -> torch.Tensor:
+        """rank-major [P, B, S_l, *row] -> [B, S, *row] (concat along the sequence, keep [0, S))."""
+        self._on_device(x, out)
+        P, B, S_l = x.shape[:3]
+        row = tuple(x.shape[3:])
+        if not x.is_contiguous() or P != self.world_size:
+            raise ValueError("x must be contiguous with P = %d rank slabs" % self.world_size)
+        if out is None:
+            out = torch.empty((B, S) + row, dtype=x.dtype, device=x.device)
+        self._check_out(out, x.dtype, B * S * math.prod(row), "seq_unshard_trim")
+        check(self._lib.uly_seq_unshard_trim(self._h(), x.data_ptr(), _dtype_code(x), B, S, math.prod(row),
+                                             S_l, out.data_ptr(), _stream_handle(stream)), "uly_seq_unshard_trim")
+        return out
+
+    # -- spatial height shards ----------------------------------------------------
+    def spatial_split_halo(self, full: torch.Tensor, halo: int = 1, out=None, stream=None) -> torch.Tensor:
+        """full [..., Hh, W] -> shards [P, ..., hmax + 2*halo, W]."""
+        self._on_device(full, out)
+        if not full.is_contiguous():
+            raise ValueError("full must be contiguous")
+        lead, (Hh, W) = tuple(full.shape[:-2]), tuple(full.shape[-2:])
+        _, hmax = height_split(Hh, self.world_size)
+        if out is None:
+            out = torch.empty((self.world_size,) + lead + (hmax + 2 * halo, W), dtype=full.dtype,
+                              device=full.device)
+        self._check_out(out, full.dtype, self.world_size * math.prod(lead) * (hmax + 2 * halo) * W,
+                        "spatial_split_halo")
+        check(self._lib.uly_spatial_split_halo(self._h(), full.data_ptr(), _dtype_code(full), math.prod(lead),
+                                               Hh, W, halo, out.data_ptr(), _stream_handle(stream)),
+              "uly_spatial_split_halo")
+        return out
+
+    def spatial_gather_stacked(self, shards: torch.Tensor, Hh: int, halo: int = 1, out=None,
+                               stream=None) -> torch.Tensor:
+        """shards [P, ..., hmax + 2*halo, W] -> stacked core rows [P, ..., hmax, W] (zero-padded)."""
+        self._on_device(shards, out)
+        lead, W = tuple(shards.shape[1:-2]), shards.shape[-1]
+        _, hmax = height_split(Hh, self.world_size)
+        if (not shards.is_contiguous() or shards.shape[0] != self.world_size
+                or shards.shape[-2] != hmax + 2 * halo):
+            raise ValueError("shards must be contiguous [P, ..., hmax + 2*halo, W]")
+        if out is None:
+            out = torch.empty((self.world_size,) + lead + (hmax, W), dtype=shards.dtype, device=shards.device)
+        self._check_out(out, shards.dtype, self.world_size * math.prod(lead) * hmax * W,
+                        "spatial_gather_stacked")
+        check(self._lib.uly_spatial_gather_stacked(self._h(), shards.data_ptr(), _dtype_code(shards),
+                                                   math.prod(lead), Hh, W, halo, out.data_ptr(),
+                                                   _stream_handle(stream)), "uly_spatial_gather_stacked")
+        return out
+
+    def spatial_trim_concat(self, stacked: torch.Tensor, Hh: int, out=None, stream=None) -> torch.Tensor:
+        """stacked [P, ..., hmax, W] -> full [..., Hh, W]."""
+        self._on_device(stacked, out)
+        lead, W = tuple(stacked.shape[1:-2]), stacked.shape[-1]
+        _, hmax = height_split(Hh, self.world_size)
+        if (not stacked.is_contiguous() or stacked.shape[0] != self.world_size
+                or stacked.shape[-2] != hmax):
+            raise ValueError("stacked must be contiguous [P, ..., hmax, W]")
+        if out is None:
+            out = torch.empty(lead + (Hh, W), dtype=stacked.dtype, device=stacked.device)
+        self._check_out(out, stacked.dtype, math.prod(lead) * Hh * W, "spatial_trim_concat")
+        check(self._lib.uly_spatial_trim_concat(self._h(), stacked.data_ptr(), _dtype_code(stacked),
+                                                math.prod(lead), Hh, W, out.data_ptr(), _stream_handle(stream)),
+              "uly_spatial_trim_concat")
+        return out
+
+    # -- measurement --------------------------------------------------------------
+    def profile(self, on: bool = True) -> None:
+        check(self._lib.uly_profile_enable(self._h(), int(bool(on))), "uly_profile_enable")
+
+    def profile_read(self, kind: str):
+        """(summed kernel ms, launches) of one kernel kind since the last reset."""
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        check(self._lib.uly_profile_read(self._h(), _lib.KERNEL_KINDS[kind], ctypes.byref(ms), ctypes.byref(n)),
+              "uly_profile_read")
+        return ms.value, n.value
+
+    def profile_reset(self) -> None:
+        check(self._lib.uly_profile_reset(self._h()), "uly_profile_reset")
+
+    def stats(self) -> dict:
+        s = _lib.UlyStats()
+        check(self._lib.uly_get_stats(self._h(), ctypes.byref(s)), "uly_get_stats")
+        return {f: getattr(s, f) for f, _ in s._fields_}
+
+    def target_count(self) -> int:
+        n = ctypes.c_int()
+        check(self._lib.uly_target_count(self._h(), ctypes.byref(n)), "uly_target_count")
+        return n.value
+
+    def comm_stream_handle(self) -> int:
+        h = ctypes.c_void_p()
+        check(self._lib.uly_comm_stream(self._h(), ctypes.byref(h)), "uly_comm_stream")
+        return h.value or 0
+
+    def debug_fail_launch(self, after: int = 0) -> None:
+        check(self._lib.uly_debug_fail_launch(self._h(), int(after)), "uly_debug_fail_launch")

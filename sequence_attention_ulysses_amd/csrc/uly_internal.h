@@ -1,0 +1,116 @@
+// Private declarations shared by the host runtime (uly_runtime.cpp) and the
+// gfx950 kernels (uly_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "fastdiv.h"
+
+namespace uly {
+
+// ---------------------------------------------------------------------------
+// Chunk relayout.  A Ulysses exchange moves contiguous chunks of Hl*D
+// elements (one token's head band) between two 4-D index spaces.  The
+// destination is always dense in the plan's iteration order, so a thread's
+// flat 16-byte vector index i gives its destination directly (dst + 16*i)
+// and its source through the 4 outer indices (i0 outermost) and the vector
+// position c inside the chunk:
+//   i = (((i0*n1 + i1)*n2 + i2)*n3 + i3)*vpc + c
+//   src = base + i0*ss[0] + i1*ss[1] + i2*ss[2] + i3*ss[3] + 16*c   (bytes)
+// ---------------------------------------------------------------------------
+struct CopyPlan {
+    const uint8_t *src;
+    uint8_t *dst;
+    int64_t ss[4];
+    FastDiv vpc;         // 16-byte vectors per chunk
+    FastDiv n3, n2, n1;  // extents of the inner three outer dims
+    uint32_t total;      // vectors in this plan
+    uint32_t first_block;
+};
+
+constexpr int kMaxPlans = 3;
+
+struct CopyBatch {
+    CopyPlan p[kMaxPlans];
+    int n;
+    uint32_t blocks;
+};
+
+// ---------------------------------------------------------------------------
+// Fused RMSNorm + RoPE + scatter.  Rows are (r, b, s, hh) in source order,
+// hh in [0, H0 + H1): hh < H0 reads operand 0 (Q), the rest operand 1 (K),
+// so one token's Q and K heads are consecutive rows and share one table row.
+// ---------------------------------------------------------------------------
+struct NormRopeOperand {
+    const uint16_t *src;
+    uint16_t *dst;
+    const uint16_t *w;
+    int64_t s_rank, s_b, s_s, s_h;   // source element strides
+    int64_t d_q, d_b, d_g;           // destination element strides (rank, batch, global token)
+    FastDiv hl;                      // heads per rank
+    uint32_t H;
+    uint32_t pad;
+};
+
+struct NormRopeArgs {
+    NormRopeOperand op[2];
+    const float *cos_tab;
+    const float *sin_tab;
+    FastDiv rpt;        // rows per token = H0 + H1
+    FastDiv sl;         // S_l
+    FastDiv bdiv;       // B
+    uint32_t H0;        // rows of operand 0 per token (0 when absent)
+    uint32_t rows;      // P*B*S_l*(H0+H1)
+    uint32_t S_l;
+    uint32_t D;
+    uint32_t rows_per_block;
+    float eps;
+    float inv_D;
+};
+
+// ---------------------------------------------------------------------------
+// Row maps with zero fill: sequence pad/trim and the spatial height shards.
+// Each destination row of `vpr` 16-byte vectors is copied from one source
+// row or zero-filled.
+// ---------------------------------------------------------------------------
+enum RowMapKind : int {
+    kPadShard = 0,       // dst x[P][B][S_l] rows  <- full[B][S] rows, zero past S
+    kUnshardTrim = 1,    // dst full[B][S] rows    <- x[P][B][S_l] rows
+    kSplitHalo = 2,      // dst sh[P][N][hmax+2h]  <- full[N][Hh], zero outside
+    kGatherStacked = 3,  // dst st[P][N][hmax]     <- sh[P][N][hmax+2h] core rows
+    kTrimConcat = 4      // dst full[N][Hh]        <- st[P][N][hmax]
+};
+
+struct RowMapArgs {
+    const uint8_t *src;
+    uint8_t *dst;
+    FastDiv vpr;         // 16-byte vectors per row
+    FastDiv f0;          // innermost destination row dimension
+    FastDiv f1;          // next destination row dimension
+    FastDiv f2;          // mode-specific: S_l (unshard) or base_h + 1 (trim/concat)
+    FastDiv f3;          // mode-specific: base_h (trim/concat)
+    uint32_t total;      // vectors written
+    uint32_t B_or_N;     // batch (pad/trim) or flattened leading dims N (spatial)
+    uint32_t S;          // pad/trim: real sequence length; spatial: Hh
+    uint32_t S_l;        // pad/trim: rows per rank; spatial: hmax
+    uint32_t halo;
+    uint32_t base_h;     // spatial: floor(Hh / P)
+    uint32_t extra_h;    // spatial: Hh % P
+    uint32_t pad;
+};
+
+// Launch wrappers (uly_kernels.hip).  They only enqueue; the caller checks
+// hipGetLastError().
+void launch_relayout(const CopyBatch &b, hipStream_t stream);
+void launch_norm_rope(const NormRopeArgs &a, int lanes, int dtype, uint32_t blocks, hipStream_t stream);
+void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
+
+constexpr int kThreads = 256;
+constexpr int kCopyUnroll = 4;                           // 16-byte vectors per thread
+constexpr uint32_t kCopyVecsPerBlock = kThreads * kCopyUnroll;
+constexpr int kRopeUnroll = 4;                           // rows in flight per lane group
+constexpr int kRopeItersPerBlock = 2;                    // unrolled passes per block
+
+}  // namespace uly

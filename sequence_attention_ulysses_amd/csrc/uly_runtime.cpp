@@ -1,0 +1,956 @@
+// Host runtime of the C ABI declared in include/uly.h: argument checks, the
+// tagged target cache, the comm stream and the grouped completion
+// handshake, launch bookkeeping and per-kernel event timing.
+//
+// Pages cited (by title and section):
+//  [CA]  TeleFuser documentation, "Communication Architecture" — "Ulysses"
+//        (the maps and their divisibility checks, done before any
+//        communication), "Stream ordering protocol" and "Efficiency
+//        Invariants" (stream events instead of device-wide syncs, Q/K/V all
+//        submitted before anyone waits).
+//  [P27] TeleFuser PR #27, "Changes Made" (cached targets keyed by tag,
+//        shape, dtype, mode and device, up to 12; one grouped handshake;
+//        V submitted before Q/K norm and RoPE) and "Description".
+//  [UC]  flashinfer UlyssesCommunicator(backend="pcie") PR, "Failure
+//        envelope" (argument rejections decided before native work, fail-
+//        stop after a transport failure) and "element type".
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "uly.h"
+#include "uly_internal.h"
+
+using namespace uly;
+
+namespace {
+
+thread_local std::string g_err;
+
+uly_status fail(uly_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+constexpr int kMaxTargetsCap = 12;   // [P27 "Changes Made"]
+constexpr int kTagMax = 63;
+constexpr int64_t kMaxVecs = int64_t(1) << 31;   // per launch plan, keeps 32-bit indexing exact
+
+struct Target {
+    std::string tag;
+    int mode;
+    int dtype;
+    int64_t shape[4];
+    int device;
+    void *ptr;
+    size_t bytes;
+};
+
+struct Pending {
+    hipStream_t stream;
+    hipEvent_t ev;
+};
+
+struct ProfRecord {
+    int kind;
+    hipEvent_t start;
+    hipEvent_t stop;
+    double ms;     // < 0 until measured
+};
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo = 0, hi = 0;   // [lo, hi), empty when lo == hi
+    bool overlaps(const Range &o) const { return lo < hi && o.lo < o.hi && lo < o.hi && o.lo < hi; }
+};
+
+// A checked rank-major 4-D operand.
+struct Operand {
+    const uint8_t *data = nullptr;
+    int dtype = 0;
+    int64_t rank_stride = 0;
+    int64_t B = 0, S = 0, H = 0, D = 0;
+    int64_t sb = 0, ss = 0, sh = 0;   // element strides
+    Range range;
+    bool empty() const { return B == 0 || S == 0; }
+};
+
+uly_status check_operand(const uly_tensor *t, const char *name, int P, Operand &o) {
+    if (!t) return fail(ULY_E_INVAL, "%s: null descriptor", name);
+    if (t->dtype != ULY_F16 && t->dtype != ULY_BF16)
+        return fail(ULY_E_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+    if (t->reserved != 0) return fail(ULY_E_INVAL, "%s: reserved field must be 0", name);
+    for (int i = 0; i < 4; ++i)
+        if (t->shape[i] < 0) return fail(ULY_E_INVAL, "%s: negative extent in dim %d", name, i);
+    if (t->shape[2] < 1 || t->shape[3] < 1)
+        return fail(ULY_E_INVAL, "%s: H and D must be positive", name);
+    if (t->stride[3] != 1) return fail(ULY_E_INVAL, "%s: head-dim stride must be 1", name);
+    if (t->rank_stride < 0 || t->stride[0] < 0 || t->stride[1] < 0 || t->stride[2] < 0)
+        return fail(ULY_E_INVAL, "%s: negative stride", name);
+    if ((t->shape[3] * 2) % 16 != 0)
+        return fail(ULY_E_INVAL, "%s: D * 2 bytes (%lld) is not a multiple of 16", name,
+                    (long long)(t->shape[3] * 2));
+    const int64_t ext[4] = {P, t->shape[0], t->shape[1], t->shape[2]};
+    const int64_t str[4] = {t->rank_stride, t->stride[0], t->stride[1], t->stride[2]};
+    for (int i = 0; i < 4; ++i)
+        if (ext[i] > 1 && (str[i] * 2) % 16 != 0)
+            return fail(ULY_E_INVAL, "%s: byte stride of dim %d (%lld) is not a multiple of 16", name,
+                        i, (long long)(str[i] * 2));
+    o.data = static_cast<const uint8_t *>(t->data);
+    o.dtype = t->dtype;
+    o.rank_stride = t->rank_stride;
+    o.B = t->shape[0];
+    o.S = t->shape[1];
+    o.H = t->shape[2];
+    o.D = t->shape[3];
+    o.sb = t->stride[0];
+    o.ss = t->stride[1];
+    o.sh = t->stride[2];
+    if (!o.empty()) {
+        if (!o.data) return fail(ULY_E_INVAL, "%s: null data pointer", name);
+        if (!aligned16(o.data)) return fail(ULY_E_INVAL, "%s: data pointer not 16-byte aligned", name);
+        int64_t maxoff = o.D - 1;
+        for (int i = 0; i < 4; ++i) maxoff += (ext[i] - 1) * str[i];
+        o.range.lo = reinterpret_cast<uintptr_t>(o.data);
+        o.range.hi = o.range.lo + uintptr_t(maxoff + 1) * 2u;
+    }
+    return ULY_OK;
+}
+
+Range dense_range(const void *p, int64_t elems) {
+    Range r;
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + uintptr_t(elems) * 2u;
+    return r;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    int dev;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int d) : dev(d) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+    }
+    ~DeviceGuard() {
+        if (prev >= 0 && prev != dev) (void)hipSetDevice(prev);
+    }
+};
+
+}  // namespace
+
+struct uly_ctx {
+    int device = -1;
+    int P = 1;
+    int max_targets = kMaxTargetsCap;
+    bool host_only = true;
+    bool broken = false;
+    hipStream_t comm = nullptr;
+    hipEvent_t fork_ev = nullptr;
+    std::vector<Target> targets;
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> sync_pool;
+    bool profiling = false;
+    std::vector<ProfRecord> prof;
+    std::vector<hipEvent_t> timing_pool;
+    uly_stats stats{};
+    int fail_after = -1;
+};
+
+namespace {
+
+uly_status ctx_ok(uly_ctx *c) {
+    if (!c) return fail(ULY_E_INVAL, "null context");
+    if (c->broken) return fail(ULY_E_BROKEN, "context is broken by an earlier failure; destroy it");
+    return ULY_OK;
+}
+
+uly_status poison(uly_ctx *c, hipError_t e, const char *what) {
+    c->broken = true;
+    return fail(ULY_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_tag(const char *tag) { return tag && tag[0] && strlen(tag) <= size_t(kTagMax); }
+
+Target *find_target(uly_ctx *c, const char *tag, int mode, int dtype, const int64_t shape[4]) {
+    for (auto &t : c->targets)
+        if (t.mode == mode && t.dtype == dtype && t.device == c->device && t.tag == tag &&
+            t.shape[0] == shape[0] && t.shape[1] == shape[1] && t.shape[2] == shape[2] &&
+            t.shape[3] == shape[3])
+            return &t;
+    return nullptr;
+}
+
+// Destination of one member: explicit pointer or the cached target of its key.
+uly_status resolve_target(uly_ctx *c, const char *name, const char *tag, void *explicit_out,
+                          int mode, int dtype, const int64_t shape[4], uint8_t *&out) {
+    if (explicit_out) {
+        if (!aligned16(explicit_out)) return fail(ULY_E_INVAL, "%s: destination not 16-byte aligned", name);
+        out = static_cast<uint8_t *>(explicit_out);
+        return ULY_OK;
+    }
+    if (!valid_tag(tag)) return fail(ULY_E_INVAL, "%s: no destination and no valid tag", name);
+    c->stats.lookups++;
+    Target *t = find_target(c, tag, mode, dtype, shape);
+    if (!t) {
+        // A tag registered with another dtype is a dtype error, not a miss ([UC] "element type").
+        for (auto &o : c->targets)
+            if (o.tag == tag && o.mode == mode && o.dtype != dtype && o.shape[0] == shape[0] &&
+                o.shape[1] == shape[1] && o.shape[2] == shape[2] && o.shape[3] == shape[3])
+                return fail(ULY_E_DTYPE, "%s: target '%s' is registered with dtype %d, call uses %d",
+                            name, tag, o.dtype, dtype);
+        return fail(ULY_E_NOT_FOUND,
+                    "%s: no target registered for tag '%s' mode %d dtype %d shape [%lld,%lld,%lld,%lld]",
+                    name, tag, mode, dtype, (long long)shape[0], (long long)shape[1],
+                    (long long)shape[2], (long long)shape[3]);
+    }
+    c->stats.hits++;
+    out = static_cast<uint8_t *>(t->ptr);
+    return ULY_OK;
+}
+
+hipEvent_t take_event(std::vector<hipEvent_t> &pool, unsigned flags, hipError_t &err) {
+    if (!pool.empty()) {
+        hipEvent_t e = pool.back();
+        pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    err = hipEventCreateWithFlags(&e, flags);
+    return err == hipSuccess ? e : nullptr;
+}
+
+// Fault injection (uly_debug_fail_launch): true when this launch must fail.
+bool injected_failure(uly_ctx *c) {
+    if (c->fail_after == 0) {
+        c->fail_after = -1;
+        c->broken = true;
+        fail(ULY_E_HIP, "injected launch failure (test hook)");
+        return true;
+    }
+    if (c->fail_after > 0) --c->fail_after;
+    return false;
+}
+
+// What a host-only context returns where a device context would launch.
+uly_status host_only_launch(uly_ctx *c) {
+    if (injected_failure(c)) return ULY_E_HIP;
+    return fail(ULY_E_UNSUPPORTED, "host-only context cannot launch");
+}
+
+// Enqueue one kernel through `enqueue`, with optional timing events and the
+// fail-stop bookkeeping.
+template <class F>
+uly_status launch(uly_ctx *c, int kind, hipStream_t s, F &&enqueue) {
+    if (injected_failure(c)) return ULY_E_HIP;
+    (void)hipGetLastError();   // clear a stale error left by someone else's call
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t err = hipSuccess;
+    if (c->profiling) {
+        e0 = take_event(c->timing_pool, hipEventDefault, err);
+        if (!e0) return poison(c, err, "hipEventCreate");
+        e1 = take_event(c->timing_pool, hipEventDefault, err);
+        if (!e1) return poison(c, err, "hipEventCreate");
+        if ((err = hipEventRecord(e0, s)) != hipSuccess) return poison(c, err, "hipEventRecord");
+    }
+    enqueue();
+    err = hipGetLastError();
+    if (err != hipSuccess) return poison(c, err, "kernel launch");
+    if (c->profiling) {
+        if ((err = hipEventRecord(e1, s)) != hipSuccess) return poison(c, err, "hipEventRecord");
+        c->prof.push_back({kind, e0, e1, -1.0});
+    }
+    c->stats.launches++;
+    return ULY_OK;
+}
+
+// Record that `s` carries work of the current group (one event per stream).
+uly_status mark_pending(uly_ctx *c, hipStream_t s) {
+    hipError_t err = hipSuccess;
+    for (auto &p : c->pending)
+        if (p.stream == s) {
+            err = hipEventRecord(p.ev, s);
+            return err == hipSuccess ? ULY_OK : poison(c, err, "hipEventRecord");
+        }
+    hipEvent_t e = take_event(c->sync_pool, hipEventDisableTiming, err);
+    if (!e) return poison(c, err, "hipEventCreate");
+    c->pending.push_back({s, e});
+    err = hipEventRecord(e, s);
+    return err == hipSuccess ? ULY_OK : poison(c, err, "hipEventRecord");
+}
+
+// The comm stream waits for everything enqueued on `caller` so far (input
+// readiness and the reuse hazard of the targets it is about to overwrite).
+uly_status fork_comm(uly_ctx *c, hipStream_t caller) {
+    hipError_t err = hipEventRecord(c->fork_ev, caller);
+    if (err != hipSuccess) return poison(c, err, "hipEventRecord");
+    err = hipStreamWaitEvent(c->comm, c->fork_ev, 0);
+    return err == hipSuccess ? ULY_OK : poison(c, err, "hipStreamWaitEvent");
+}
+
+// Plan of one scatter member: rank-major source [P][B][S_l][H][D] (strided)
+// -> dense [P(q)][B][P(r)*S_l][Hl][D]; iteration (q, b, r, s, chunk vector).
+uly_status plan_scatter(const Operand &x, int P, uint8_t *dst, CopyPlan &p) {
+    const int64_t Hl = x.H / P;
+    const int64_t chunk_bytes = Hl * x.D * 2;
+    const int64_t vpc = chunk_bytes / 16;
+    const int64_t total = int64_t(P) * x.B * P * x.S * vpc;
+    if (total >= kMaxVecs || x.S >= kMaxVecs || x.B >= kMaxVecs)
+        return fail(ULY_E_UNSUPPORTED, "operand too large for one launch (%lld vectors)", (long long)total);
+    p = CopyPlan{};
+    p.src = x.data;
+    p.dst = dst;
+    p.ss[0] = Hl * x.sh * 2;          // q: head band offset
+    p.ss[1] = x.sb * 2;               // b
+    p.ss[2] = x.rank_stride * 2;      // r: source rank slab
+    p.ss[3] = x.ss * 2;               // s
+    p.vpc = FastDiv::make(uint32_t(vpc));
+    p.n1 = FastDiv::make(uint32_t(x.B));
+    p.n2 = FastDiv::make(uint32_t(P));
+    p.n3 = FastDiv::make(uint32_t(x.S));
+    p.total = uint32_t(total);
+    return ULY_OK;
+}
+
+// Plan of the inverse: head-sharded [P(q)][B][S][Hl][D] (strided) -> dense
+// [P(r)][B][S_l][P(q)*Hl][D]; iteration (r, b, s, q, chunk vector).
+uly_status plan_gather(const Operand &o, int P, uint8_t *dst, CopyPlan &p) {
+    const int64_t S_l = o.S / P;
+    const int64_t chunk_bytes = o.H * o.D * 2;
+    const int64_t vpc = chunk_bytes / 16;
+    const int64_t total = int64_t(P) * o.B * S_l * P * vpc;
+    if (total >= kMaxVecs || o.S >= kMaxVecs || o.B >= kMaxVecs)
+        return fail(ULY_E_UNSUPPORTED, "operand too large for one launch (%lld vectors)", (long long)total);
+    p = CopyPlan{};
+    p.src = o.data;
+    p.dst = dst;
+    p.ss[0] = S_l * o.ss * 2;         // r: destination rank's sequence block
+    p.ss[1] = o.sb * 2;               // b
+    p.ss[2] = o.ss * 2;               // s
+    p.ss[3] = o.rank_stride * 2;      // q: source rank slab (head band)
+    p.vpc = FastDiv::make(uint32_t(vpc));
+    p.n1 = FastDiv::make(uint32_t(o.B));
+    p.n2 = FastDiv::make(uint32_t(S_l));
+    p.n3 = FastDiv::make(uint32_t(P));
+    p.total = uint32_t(total);
+    return ULY_OK;
+}
+
+uly_status finish_batch(CopyBatch &b) {
+    uint64_t blocks = 0;
+    for (int i = 0; i < b.n; ++i) {
+        b.p[i].first_block = uint32_t(blocks);
+        blocks += (b.p[i].total + kCopyVecsPerBlock - 1) / kCopyVecsPerBlock;
+    }
+    if (blocks >= (uint64_t(1) << 31)) return fail(ULY_E_UNSUPPORTED, "grid too large");
+    b.blocks = uint32_t(blocks);
+    return ULY_OK;
+}
+
+uly_status check_overlaps(const std::vector<Range> &in, const std::vector<Range> &out) {
+    for (size_t i = 0; i < out.size(); ++i) {
+        for (const Range &r : in)
+            if (out[i].overlaps(r)) return fail(ULY_E_OVERLAP, "an input overlaps destination %zu", i);
+        for (size_t j = i + 1; j < out.size(); ++j)
+            if (out[i].overlaps(out[j])) return fail(ULY_E_OVERLAP, "destinations %zu and %zu overlap", i, j);
+    }
+    return ULY_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char *uly_last_error(void) { return g_err.c_str(); }
+
+const char *uly_status_string(int st) {
+    switch (st) {
+    case ULY_OK: return "ULY_OK";
+    case ULY_E_INVAL: return "ULY_E_INVAL";
+    case ULY_E_DTYPE: return "ULY_E_DTYPE";
+    case ULY_E_CACHE_FULL: return "ULY_E_CACHE_FULL";
+    case ULY_E_NOT_FOUND: return "ULY_E_NOT_FOUND";
+    case ULY_E_UNSUPPORTED: return "ULY_E_UNSUPPORTED";
+    case ULY_E_HIP: return "ULY_E_HIP";
+    case ULY_E_BROKEN: return "ULY_E_BROKEN";
+    case ULY_E_OVERLAP: return "ULY_E_OVERLAP";
+    default: return "unknown status";
+    }
+}
+
+uly_status uly_create(uly_ctx **out, int device, int world_size, int max_targets) {
+    if (!out) return fail(ULY_E_INVAL, "null output pointer");
+    *out = nullptr;
+    if (world_size < 1) return fail(ULY_E_INVAL, "world_size must be >= 1 (got %d)", world_size);
+    if (max_targets < 1 || max_targets > kMaxTargetsCap)
+        return fail(ULY_E_INVAL, "max_targets must be in [1, %d] (got %d)", kMaxTargetsCap, max_targets);
+    if (device < -1) return fail(ULY_E_INVAL, "device must be >= -1 (got %d)", device);
+    uly_ctx *c = new uly_ctx();
+    c->device = device;
+    c->P = world_size;
+    c->max_targets = max_targets;
+    c->host_only = device < 0;
+    if (!c->host_only) {
+        int n = 0;
+        hipError_t err = hipGetDeviceCount(&n);
+        if (err != hipSuccess || device >= n) {
+            delete c;
+            return err != hipSuccess ? fail(ULY_E_HIP, "hipGetDeviceCount: %s", hipGetErrorString(err))
+                                     : fail(ULY_E_INVAL, "device %d out of range (%d devices)", device, n);
+        }
+        DeviceGuard g(device);
+        if (g.err != hipSuccess) {
+            delete c;
+            return fail(ULY_E_HIP, "hipSetDevice: %s", hipGetErrorString(g.err));
+        }
+        // Default priority on purpose: the overlap comes from two streams,
+        // not from a priority difference.
+        err = hipStreamCreateWithFlags(&c->comm, hipStreamNonBlocking);
+        if (err == hipSuccess) err = hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming);
+        if (err != hipSuccess) {
+            if (c->comm) (void)hipStreamDestroy(c->comm);
+            delete c;
+            return fail(ULY_E_HIP, "stream/event creation: %s", hipGetErrorString(err));
+        }
+    }
+    *out = c;
+    return ULY_OK;
+}
+
+uly_status uly_destroy(uly_ctx *c) {
+    if (!c) return ULY_OK;
+    uly_status st = ULY_OK;
+    if (!c->host_only) {
+        DeviceGuard g(c->device);
+        if (c->comm && hipStreamSynchronize(c->comm) != hipSuccess)
+            st = fail(ULY_E_HIP, "hipStreamSynchronize on destroy failed");
+        for (auto &p : c->pending) (void)hipEventDestroy(p.ev);
+        for (auto e : c->sync_pool) (void)hipEventDestroy(e);
+        for (auto &r : c->prof) {
+            (void)hipEventDestroy(r.start);
+            (void)hipEventDestroy(r.stop);
+        }
+        for (auto e : c->timing_pool) (void)hipEventDestroy(e);
+        if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
+        if (c->comm) (void)hipStreamDestroy(c->comm);
+    }
+    delete c;
+    return st;
+}
+
+uly_status uly_target_register(uly_ctx *c, const char *tag, int mode, int dtype, const int64_t shape[4],
+                               void *storage, size_t bytes) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    if (!valid_tag(tag)) return fail(ULY_E_INVAL, "tag must be 1..%d bytes", kTagMax);
+    if (mode != ULY_MODE_SCATTER && mode != ULY_MODE_GATHER) return fail(ULY_E_INVAL, "bad mode %d", mode);
+    if (dtype != ULY_F16 && dtype != ULY_BF16) return fail(ULY_E_DTYPE, "bad dtype %d", dtype);
+    if (!shape) return fail(ULY_E_INVAL, "null shape");
+    int64_t elems = c->P;
+    for (int i = 0; i < 4; ++i) {
+        if (shape[i] < 1) return fail(ULY_E_INVAL, "target extents must be positive");
+        elems *= shape[i];
+    }
+    if (!storage || !aligned16(storage)) return fail(ULY_E_INVAL, "storage null or not 16-byte aligned");
+    if (bytes < size_t(elems) * 2u)
+        return fail(ULY_E_INVAL, "storage of %zu bytes is smaller than the %lld bytes of P slabs", bytes,
+                    (long long)(elems * 2));
+    if (find_target(c, tag, mode, dtype, shape))
+        return fail(ULY_E_INVAL, "target '%s' with this key is already registered", tag);
+    if (int(c->targets.size()) >= c->max_targets)
+        return fail(ULY_E_CACHE_FULL, "target cache holds its maximum of %d entries", c->max_targets);
+    Target t;
+    t.tag = tag;
+    t.mode = mode;
+    t.dtype = dtype;
+    for (int i = 0; i < 4; ++i) t.shape[i] = shape[i];
+    t.device = c->device;
+    t.ptr = storage;
+    t.bytes = bytes;
+    c->targets.push_back(t);
+    c->stats.registrations++;
+    return ULY_OK;
+}
+
+uly_status uly_target_lookup(uly_ctx *c, const char *tag, int mode, int dtype, const int64_t shape[4],
+                             void **storage) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    if (!storage || !shape || !valid_tag(tag)) return fail(ULY_E_INVAL, "bad lookup arguments");
+    *storage = nullptr;
+    c->stats.lookups++;
+    Target *t = find_target(c, tag, mode, dtype, shape);
+    if (!t) return fail(ULY_E_NOT_FOUND, "no target for tag '%s'", tag);
+    c->stats.hits++;
+    *storage = t->ptr;
+    return ULY_OK;
+}
+
+uly_status uly_target_count(uly_ctx *c, int *count) {
+    if (!c || !count) return fail(ULY_E_INVAL, "null argument");
+    *count = int(c->targets.size());
+    return ULY_OK;
+}
+
+uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor *k, const uly_tensor *v,
+                               const char *const tags[3], void *const outs[3], hipStream_t caller) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    const uly_tensor *mem[3] = {q, k, v};
+    const char *names[3] = {"q", "k", "v"};
+    Operand ops[3];
+    int present = 0, dtype = 0;
+    int64_t B = -1, S = -1, D = -1;
+    std::vector<Range> in_ranges, out_ranges;
+    CopyBatch batch{};
+    // Every member is checked and resolved before anything is enqueued.
+    for (int i = 0; i < 3; ++i) {
+        if (!mem[i]) continue;
+        if ((st = check_operand(mem[i], names[i], c->P, ops[i])) != ULY_OK) return st;
+        const Operand &x = ops[i];
+        if (x.H % c->P != 0)
+            return fail(ULY_E_INVAL, "%s: heads %lld not divisible by world size %d", names[i],
+                        (long long)x.H, c->P);
+        const int64_t Hl = x.H / c->P;
+        if (Hl > 1 && x.sh != x.D)
+            return fail(ULY_E_INVAL, "%s: heads of a token must be packed (stride[2] == D)", names[i]);
+        if (present == 0) {
+            dtype = x.dtype; B = x.B; S = x.S; D = x.D;
+        } else {
+            if (x.dtype != dtype) return fail(ULY_E_DTYPE, "%s: dtype differs from the other members", names[i]);
+            if (x.B != B || x.S != S || x.D != D)
+                return fail(ULY_E_INVAL, "%s: B, S_l and D must match the other members", names[i]);
+        }
+        ++present;
+        const int64_t tshape[4] = {x.B, x.S * c->P, Hl, x.D};
+        uint8_t *dst = nullptr;
+        if (x.empty()) continue;
+        if ((st = resolve_target(c, names[i], tags ? tags[i] : nullptr, outs ? outs[i] : nullptr,
+                                 ULY_MODE_SCATTER, x.dtype, tshape, dst)) != ULY_OK)
+            return st;
+        in_ranges.push_back(x.range);
+        out_ranges.push_back(dense_range(dst, int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3]));
+        if ((st = plan_scatter(x, c->P, dst, batch.p[batch.n])) != ULY_OK) return st;
+        batch.n++;
+    }
+    if (present == 0) return fail(ULY_E_INVAL, "no operand given");
+    if ((st = check_overlaps(in_ranges, out_ranges)) != ULY_OK) return st;
+    if ((st = finish_batch(batch)) != ULY_OK) return st;
+    if (c->host_only) return host_only_launch(c);
+    if (batch.n == 0) return ULY_OK;
+    DeviceGuard g(c->device);
+    if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
+    if ((st = fork_comm(c, caller)) != ULY_OK) return st;
+    if ((st = launch(c, ULY_K_SCATTER, c->comm, [&] { launch_relayout(batch, c->comm); })) != ULY_OK)
+        return st;
+    return mark_pending(c, c->comm);
+}
+
+uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly_tensor *k, const void *w_q,
+                                      const void *w_k, float eps, const float *cos_tab,
+                                      const float *sin_tab, int64_t table_rows, const char *const tags[2],
+                                      void *const outs[2], hipStream_t caller) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    const uly_tensor *mem[2] = {q, k};
+    const void *wts[2] = {w_q, w_k};
+    const char *names[2] = {"q", "k"};
+    Operand ops[2];
+    uint8_t *dsts[2] = {nullptr, nullptr};
+    int present = 0, dtype = 0;
+    int64_t B = -1, S = -1, D = -1;
+    std::vector<Range> in_ranges, out_ranges;
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(ULY_E_INVAL, "eps must be a positive finite value");
+    for (int i = 0; i < 2; ++i) {
+        if (!mem[i]) continue;
+        if ((st = check_operand(mem[i], names[i], c->P, ops[i])) != ULY_OK) return st;
+        const Operand &x = ops[i];
+        if (x.H % c->P != 0)
+            return fail(ULY_E_INVAL, "%s: heads %lld not divisible by world size %d", names[i],
+                        (long long)x.H, c->P);
+        if (present == 0) {
+            dtype = x.dtype; B = x.B; S = x.S; D = x.D;
+        } else {
+            if (x.dtype != dtype) return fail(ULY_E_DTYPE, "%s: dtype differs from q", names[i]);
+            if (x.B != B || x.S != S || x.D != D)
+                return fail(ULY_E_INVAL, "%s: B, S_l and D must match q", names[i]);
+        }
+        ++present;
+        if (!wts[i] || !aligned16(wts[i]))
+            return fail(ULY_E_INVAL, "%s: weight pointer null or not 16-byte aligned", names[i]);
+    }
+    if (present == 0) return fail(ULY_E_INVAL, "no operand given");
+    const int lanes = int(D * 2 / 16);
+    if (D % 2 != 0 || !(lanes == 4 || lanes == 8 || lanes == 16 || lanes == 32))
+        return fail(ULY_E_UNSUPPORTED, "head dim %lld not supported (32, 64, 128 or 256)", (long long)D);
+    if (!cos_tab || !sin_tab || !aligned16(cos_tab) || !aligned16(sin_tab))
+        return fail(ULY_E_INVAL, "cos/sin tables null or not 16-byte aligned");
+    if (table_rows < int64_t(c->P) * S)
+        return fail(ULY_E_INVAL, "table has %lld rows, positions reach %lld", (long long)table_rows,
+                    (long long)(int64_t(c->P) * S));
+    for (int i = 0; i < 2; ++i) {
+        if (!mem[i] || ops[i].empty()) continue;
+        const Operand &x = ops[i];
+        const int64_t tshape[4] = {x.B, x.S * c->P, x.H / c->P, x.D};
+        if ((st = resolve_target(c, names[i], tags ? tags[i] : nullptr, outs ? outs[i] : nullptr,
+                                 ULY_MODE_SCATTER, x.dtype, tshape, dsts[i])) != ULY_OK)
+            return st;
+        in_ranges.push_back(x.range);
+        out_ranges.push_back(dense_range(dsts[i], int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3]));
+    }
+    in_ranges.push_back(dense_range(cos_tab, table_rows * D));   // fp32 [rows][D/2] = 2*rows*D/2 halves
+    in_ranges.push_back(dense_range(sin_tab, table_rows * D));
+    in_ranges.push_back(dense_range(w_q ? w_q : cos_tab, w_q ? D : 0));
+    in_ranges.push_back(dense_range(w_k ? w_k : cos_tab, w_k ? D : 0));
+    if ((st = check_overlaps(in_ranges, out_ranges)) != ULY_OK) return st;
+
+    NormRopeArgs a{};
+    uint32_t Hsum = 0;
+    for (int i = 0; i < 2; ++i) {
+        NormRopeOperand &o = a.op[i];
+        o = NormRopeOperand{};
+        o.hl = FastDiv::make(1);
+        if (!mem[i] || ops[i].empty()) continue;
+        const Operand &x = ops[i];
+        const int64_t Hl = x.H / c->P, Sg = x.S * c->P;
+        o.src = reinterpret_cast<const uint16_t *>(x.data);
+        o.dst = reinterpret_cast<uint16_t *>(dsts[i]);
+        o.w = static_cast<const uint16_t *>(wts[i]);
+        o.s_rank = x.rank_stride;
+        o.s_b = x.sb;
+        o.s_s = x.ss;
+        o.s_h = x.sh;
+        o.d_q = x.B * Sg * Hl * x.D;
+        o.d_b = Sg * Hl * x.D;
+        o.d_g = Hl * x.D;
+        o.hl = FastDiv::make(uint32_t(Hl));
+        o.H = uint32_t(x.H);
+        Hsum += uint32_t(x.H);
+    }
+    const bool has_q = mem[0] && !ops[0].empty();
+    const int64_t rows = int64_t(c->P) * B * S * Hsum;
+    if (c->host_only) return host_only_launch(c);
+    if (rows == 0) return ULY_OK;
+    if (rows >= kMaxVecs || int64_t(c->P) * S >= kMaxVecs)
+        return fail(ULY_E_UNSUPPORTED, "too many rows for one launch (%lld)", (long long)rows);
+    a.cos_tab = cos_tab;
+    a.sin_tab = sin_tab;
+    a.rpt = FastDiv::make(Hsum);
+    a.sl = FastDiv::make(uint32_t(S));
+    a.bdiv = FastDiv::make(uint32_t(B));
+    a.H0 = has_q ? a.op[0].H : 0u;
+    a.rows = uint32_t(rows);
+    a.S_l = uint32_t(S);
+    a.D = uint32_t(D);
+    const uint32_t groups = uint32_t(kThreads / lanes);
+    a.rows_per_block = groups * kRopeUnroll * kRopeItersPerBlock;
+    a.eps = eps;
+    a.inv_D = 1.0f / float(D);
+    const uint32_t blocks = uint32_t((rows + a.rows_per_block - 1) / a.rows_per_block);
+    DeviceGuard g(c->device);
+    if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
+    if ((st = launch(c, ULY_K_NORM_ROPE, caller,
+                     [&] { launch_norm_rope(a, lanes, dtype, blocks, caller); })) != ULY_OK)
+        return st;
+    return mark_pending(c, caller);
+}
+
+uly_status uly_wait(uly_ctx *c, hipStream_t consumer) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    if (c->host_only) {
+        c->pending.clear();
+        return ULY_OK;
+    }
+    DeviceGuard g(c->device);
+    if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
+    for (auto &p : c->pending) {
+        if (p.stream != consumer) {
+            hipError_t err = hipStreamWaitEvent(consumer, p.ev, 0);
+            if (err != hipSuccess) return poison(c, err, "hipStreamWaitEvent");
+        }
+        c->sync_pool.push_back(p.ev);
+    }
+    c->pending.clear();
+    return ULY_OK;
+}
+
+uly_status ulysses_gather_out(uly_ctx *c, const uly_tensor *o, const char *tag, void *out, hipStream_t caller) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    Operand x;
+    if ((st = check_operand(o, "out", c->P, x)) != ULY_OK) return st;
+    if (x.S % c->P != 0)
+        return fail(ULY_E_INVAL, "gathered sequence %lld not divisible by world size %d", (long long)x.S, c->P);
+    if (x.H > 1 && x.sh != x.D) return fail(ULY_E_INVAL, "out: heads must be packed (stride[2] == D)");
+    const int64_t tshape[4] = {x.B, x.S / c->P, x.H * c->P, x.D};
+    CopyBatch batch{};
+    if (!x.empty()) {
+        uint8_t *dst = nullptr;
+        if ((st = resolve_target(c, "out", tag, out, ULY_MODE_GATHER, x.dtype, tshape, dst)) != ULY_OK) return st;
+        std::vector<Range> in{x.range};
+        std::vector<Range> outs{dense_range(dst, int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3])};
+        if ((st = check_overlaps(in, outs)) != ULY_OK) return st;
+        if ((st = plan_gather(x, c->P, dst, batch.p[0])) != ULY_OK) return st;
+        batch.n = 1;
+    }
+    if ((st = finish_batch(batch)) != ULY_OK) return st;
+    if (c->host_only) return host_only_launch(c);
+    if (batch.n == 0) return ULY_OK;
+    DeviceGuard g(c->device);
+    if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
+    return launch(c, ULY_K_GATHER, caller, [&] { launch_relayout(batch, caller); });
+}
+
+// ---- sequence padding ------------------------------------------------------
+
+static uly_status rowmap_common(uly_ctx *c, const void *src, int dtype, int64_t row_elems, void *dst,
+                                int64_t src_rows, int64_t dst_rows, RowMapArgs &a) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    if (dtype != ULY_F16 && dtype != ULY_BF16) return fail(ULY_E_DTYPE, "bad dtype %d", dtype);
+    if (row_elems < 1 || (row_elems * 2) % 16 != 0)
+        return fail(ULY_E_INVAL, "row of %lld elements is not a positive multiple of 16 bytes",
+                    (long long)row_elems);
+    if (src_rows < 0 || dst_rows < 0) return fail(ULY_E_INVAL, "negative extent");
+    const int64_t vpr = row_elems * 2 / 16;
+    const int64_t total = dst_rows * vpr;
+    if (total >= kMaxVecs || src_rows * vpr >= kMaxVecs) return fail(ULY_E_UNSUPPORTED, "too large for one launch");
+    if (total > 0) {
+        if (!dst || !aligned16(dst)) return fail(ULY_E_INVAL, "destination null or not 16-byte aligned");
+        if (src_rows > 0 && (!src || !aligned16(src))) return fail(ULY_E_INVAL, "source null or not 16-byte aligned");
+        if (dense_range(src, src_rows * row_elems).overlaps(dense_range(dst, dst_rows * row_elems)))
+            return fail(ULY_E_OVERLAP, "source and destination overlap");
+    }
+    a = RowMapArgs{};
+    a.src = static_cast<const uint8_t *>(src);
+    a.dst = static_cast<uint8_t *>(dst);
+    a.vpr = FastDiv::make(uint32_t(vpr));
+    a.total = uint32_t(total);
+    return ULY_OK;
+}
+
+static uly_status rowmap_launch(uly_ctx *c, const RowMapArgs &a, int rkind, int pkind, hipStream_t s) {
+    if (c->host_only) return host_only_launch(c);
+    if (a.total == 0) return ULY_OK;
+    DeviceGuard g(c->device);
+    if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
+    return launch(c, pkind, s, [&] { launch_rowmap(a, rkind, s); });
+}
+
+uly_status uly_seq_pad_shard(uly_ctx *c, const void *full, int dtype, int64_t B, int64_t S, int64_t row_elems,
+                             int64_t S_l, void *x, hipStream_t stream) {
+    if (c && (B < 0 || S < 0 || S_l < 0 || int64_t(c->P) * S_l < S))
+        return fail(ULY_E_INVAL, "need B, S >= 0 and P*S_l >= S");
+    RowMapArgs a;
+    uly_status st = rowmap_common(c, full, dtype, row_elems, x, B * S, int64_t(c ? c->P : 0) * B * S_l, a);
+    if (st != ULY_OK) return st;
+    a.f0 = FastDiv::make(uint32_t(S_l));
+    a.f1 = FastDiv::make(uint32_t(B));
+    a.B_or_N = uint32_t(B);
+    a.S = uint32_t(S);
+    a.S_l = uint32_t(S_l);
+    return rowmap_launch(c, a, kPadShard, ULY_K_PAD, stream);
+}
+
+uly_status uly_seq_unshard_trim(uly_ctx *c, const void *x, int dtype, int64_t B, int64_t S, int64_t row_elems,
+                                int64_t S_l, void *full, hipStream_t stream) {
+    if (c && (B < 0 || S < 0 || S_l < 0 || int64_t(c->P) * S_l < S))
+        return fail(ULY_E_INVAL, "need B, S >= 0 and P*S_l >= S");
+    RowMapArgs a;
+    uly_status st = rowmap_common(c, x, dtype, row_elems, full, int64_t(c ? c->P : 0) * B * S_l, B * S, a);
+    if (st != ULY_OK) return st;
+    a.f0 = FastDiv::make(uint32_t(S));
+    a.f2 = FastDiv::make(uint32_t(S_l));
+    a.B_or_N = uint32_t(B);
+    a.S = uint32_t(S);
+    a.S_l = uint32_t(S_l);
+    return rowmap_launch(c, a, kUnshardTrim, ULY_K_PAD, stream);
+}
+
+// ---- spatial ---------------------------------------------------------------
+
+static uly_status spatial_dims(uly_ctx *c, int64_t N, int64_t Hh, int64_t W, int64_t halo, int64_t &hmax) {
+    if (!c) return fail(ULY_E_INVAL, "null context");
+    if (N < 0 || Hh < 1 || W < 1 || halo < 0) return fail(ULY_E_INVAL, "bad spatial extents");
+    if (Hh < c->P) return fail(ULY_E_INVAL, "height %lld smaller than world size %d", (long long)Hh, c->P);
+    hmax = (Hh + c->P - 1) / c->P;
+    if (halo > hmax) return fail(ULY_E_INVAL, "halo larger than a shard");
+    return ULY_OK;
+}
+
+static void spatial_fill(RowMapArgs &a, int P, int64_t N, int64_t Hh, int64_t hmax, int64_t halo) {
+    a.B_or_N = uint32_t(N);
+    a.S = uint32_t(Hh);
+    a.S_l = uint32_t(hmax);
+    a.halo = uint32_t(halo);
+    a.base_h = uint32_t(Hh / P);
+    a.extra_h = uint32_t(Hh % P);
+}
+
+uly_status uly_spatial_split_halo(uly_ctx *c, const void *full, int dtype, int64_t N, int64_t Hh, int64_t W,
+                                  int64_t halo, void *shards, hipStream_t stream) {
+    int64_t hmax = 0;
+    uly_status st = spatial_dims(c, N, Hh, W, halo, hmax);
+    if (st != ULY_OK) return st;
+    RowMapArgs a;
+    const int64_t R2 = hmax + 2 * halo;
+    if ((st = rowmap_common(c, full, dtype, W, shards, N * Hh, int64_t(c->P) * N * R2, a)) != ULY_OK) return st;
+    a.f0 = FastDiv::make(uint32_t(R2));
+    a.f1 = FastDiv::make(uint32_t(N));
+    spatial_fill(a, c->P, N, Hh, hmax, halo);
+    return rowmap_launch(c, a, kSplitHalo, ULY_K_SPATIAL, stream);
+}
+
+uly_status uly_spatial_gather_stacked(uly_ctx *c, const void *shards, int dtype, int64_t N, int64_t Hh,
+                                      int64_t W, int64_t halo, void *stacked, hipStream_t stream) {
+    int64_t hmax = 0;
+    uly_status st = spatial_dims(c, N, Hh, W, halo, hmax);
+    if (st != ULY_OK) return st;
+    RowMapArgs a;
+    const int64_t R2 = hmax + 2 * halo;
+    if ((st = rowmap_common(c, shards, dtype, W, stacked, int64_t(c->P) * N * R2, int64_t(c->P) * N * hmax, a)) !=
+        ULY_OK)
+        return st;
+    a.f0 = FastDiv::make(uint32_t(hmax));
+    a.f1 = FastDiv::make(uint32_t(N));
+    spatial_fill(a, c->P, N, Hh, hmax, halo);
+    return rowmap_launch(c, a, kGatherStacked, ULY_K_SPATIAL, stream);
+}
+
+uly_status uly_spatial_trim_concat(uly_ctx *c, const void *stacked, int dtype, int64_t N, int64_t Hh, int64_t W,
+                                   void *full, hipStream_t stream) {
+    int64_t hmax = 0;
+    uly_status st = spatial_dims(c, N, Hh, W, 0, hmax);
+    if (st != ULY_OK) return st;
+    RowMapArgs a;
+    if ((st = rowmap_common(c, stacked, dtype, W, full, int64_t(c->P) * N * hmax, N * Hh, a)) != ULY_OK) return st;
+    a.f0 = FastDiv::make(uint32_t(Hh));
+    a.f2 = FastDiv::make(uint32_t(Hh / c->P + 1));
+    a.f3 = FastDiv::make(uint32_t(Hh / c->P));
+    spatial_fill(a, c->P, N, Hh, hmax, 0);
+    return rowmap_launch(c, a, kTrimConcat, ULY_K_SPATIAL, stream);
+}
+
+// ---- rotary tables (host) ----------------------------------------------------
+
+uly_status uly_rope_table_1d(float *cos_out, float *sin_out, int64_t rows, int64_t real_rows, int64_t D,
+                             double theta) {
+    if (!cos_out || !sin_out || rows < 0 || real_rows < 0 || D < 2 || D % 2 || !(theta > 0))
+        return fail(ULY_E_INVAL, "bad rope table arguments");
+    const int64_t half = D / 2;
+    std::vector<double> inv_freq(half);
+    for (int64_t j = 0; j < half; ++j) inv_freq[j] = std::pow(theta, -2.0 * double(j) / double(D));
+    for (int64_t g = 0; g < rows; ++g)
+        for (int64_t j = 0; j < half; ++j) {
+            const bool real = g < real_rows;
+            const double ang = double(g) * inv_freq[j];
+            cos_out[g * half + j] = real ? float(std::cos(ang)) : 1.0f;
+            sin_out[g * half + j] = real ? float(std::sin(ang)) : 0.0f;
+        }
+    return ULY_OK;
+}
+
+uly_status uly_rope_table_3d(float *cos_out, float *sin_out, int64_t rows, int64_t real_rows, int64_t D,
+                             int64_t grid_h, int64_t grid_w, int64_t n_t, int64_t n_h, int64_t n_w, double theta) {
+    if (!cos_out || !sin_out || rows < 0 || real_rows < 0 || D < 2 || D % 2 || grid_h < 1 || grid_w < 1 ||
+        n_t < 0 || n_h < 0 || n_w < 0 || n_t + n_h + n_w > D / 2 || !(theta > 0))
+        return fail(ULY_E_INVAL, "bad 3-D rope table arguments");
+    const int64_t half = D / 2;
+    const int64_t band_start[3] = {0, n_t, n_t + n_h};
+    const int64_t band_len[3] = {n_t, n_h, n_w};
+    for (int64_t g = 0; g < rows; ++g) {
+        const int64_t coord[3] = {g / (grid_h * grid_w), (g / grid_w) % grid_h, g % grid_w};
+        for (int64_t j = 0; j < half; ++j) {
+            cos_out[g * half + j] = 1.0f;
+            sin_out[g * half + j] = 0.0f;
+        }
+        if (g >= real_rows) continue;
+        for (int axis = 0; axis < 3; ++axis)
+            for (int64_t k = 0; k < band_len[axis]; ++k) {
+                const double ang =
+                    double(coord[axis]) * std::pow(theta, -2.0 * double(k) / double(2 * band_len[axis]));
+                cos_out[g * half + band_start[axis] + k] = float(std::cos(ang));
+                sin_out[g * half + band_start[axis] + k] = float(std::sin(ang));
+            }
+    }
+    return ULY_OK;
+}
+
+// ---- measurement and test hooks ------------------------------------------------
+
+uly_status uly_profile_enable(uly_ctx *c, int on) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    c->profiling = on != 0;
+    return ULY_OK;
+}
+
+uly_status uly_profile_read(uly_ctx *c, int kind, double *total_ms, int64_t *launches) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    if (kind < 0 || kind >= ULY_K_COUNT || !total_ms || !launches) return fail(ULY_E_INVAL, "bad arguments");
+    double sum = 0;
+    int64_t n = 0;
+    for (auto &r : c->prof) {
+        if (r.kind != kind) continue;
+        if (r.ms < 0) {
+            hipError_t err = hipEventSynchronize(r.stop);
+            float ms = 0;
+            if (err == hipSuccess) err = hipEventElapsedTime(&ms, r.start, r.stop);
+            if (err != hipSuccess) return poison(c, err, "reading timing events");
+            r.ms = ms;
+        }
+        sum += r.ms;
+        ++n;
+    }
+    *total_ms = sum;
+    *launches = n;
+    return ULY_OK;
+}
+
+uly_status uly_profile_reset(uly_ctx *c) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    for (auto &r : c->prof) {
+        if (r.ms < 0) (void)hipEventSynchronize(r.stop);
+        c->timing_pool.push_back(r.start);
+        c->timing_pool.push_back(r.stop);
+    }
+    c->prof.clear();
+    return ULY_OK;
+}
+
+uly_status uly_get_stats(uly_ctx *c, uly_stats *out) {
+    if (!c || !out) return fail(ULY_E_INVAL, "null argument");
+    *out = c->stats;
+    return ULY_OK;
+}
+
+uly_status uly_comm_stream(uly_ctx *c, hipStream_t *out) {
+    if (!c || !out) return fail(ULY_E_INVAL, "null argument");
+    *out = c->comm;
+    return ULY_OK;
+}
+
+uly_status uly_debug_fail_launch(uly_ctx *c, int after) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    c->fail_after = after < 0 ? -1 : after;
+    return ULY_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,340 @@
+"""Host-only checks of the C ABI (no GPU): exported symbols, argument
+rejection before any launch, the tagged target cache, the fail-stop rule,
+the division helper and the library's rotary tables against the oracle's.
+
+A host-only context (device -1) runs every check a device context runs and
+returns ULY_E_UNSUPPORTED where it would launch; the pointers below are
+never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from sequence_attention_ulysses_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uly.h")
+BASE = 0x7F0000000000          # fake, 16-byte aligned device addresses
+MiB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported(lib):
+    names = header_functions()
+    assert "ulysses_scatter_qkv" in names and "fused_qk_norm_rope_scatter" in names
+    assert "ulysses_gather_out" in names
+    out = subprocess.check_output(["nm", "-D", "--defined-only", _lib.LIB_PATH]).decode()
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(_lib.EXPORTS) == names
+
+
+class Ctx:
+    def __init__(self, lib, P, max_targets=12):
+        self.lib = lib
+        self.h = ctypes.c_void_p()
+        assert lib.uly_create(ctypes.byref(self.h), -1, P, max_targets) == _lib.OK
+        self.P = P
+
+    def close(self):
+        assert self.lib.uly_destroy(self.h) == _lib.OK
+
+
+@pytest.fixture
+def ctx4(lib):
+    c = Ctx(lib, 4)
+    yield c
+    c.close()
+
+
+def T(addr, shape, stride=None, rank_stride=None, dtype=_lib.BF16):
+    """uly_tensor for a rank-major operand; contiguous strides by default."""
+    B, S, H, D = shape
+    if stride is None:
+        stride = (S * H * D, H * D, D, 1)
+    if rank_stride is None:
+        rank_stride = B * S * H * D
+    t = _lib.UlyTensor()
+    t.data = addr
+    t.dtype = dtype
+    t.reserved = 0
+    t.rank_stride = rank_stride
+    for i in range(4):
+        t.shape[i] = shape[i]
+        t.stride[i] = stride[i]
+    return t
+
+
+def register(lib, c, tag, mode, shape, addr, dtype=_lib.BF16, nbytes=None):
+    n = c.P * int(np.prod(shape)) * 2
+    return lib.uly_target_register(c.h, tag.encode(), mode, dtype, _lib.int64_array(shape), addr,
+                                   n if nbytes is None else nbytes)
+
+
+def scatter(lib, c, q=None, k=None, v=None, tags=("q", "k", "v"), outs=(None, None, None)):
+    args = [ctypes.byref(x) if x is not None else None for x in (q, k, v)]
+    return lib.ulysses_scatter_qkv(c.h, *args, _lib.tags_array(tags), _lib.ptr_array(outs), None)
+
+
+def test_create_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.uly_create(ctypes.byref(h), -1, 0, 12) == _lib.E_INVAL
+    assert lib.uly_create(ctypes.byref(h), -1, 4, 13) == _lib.E_INVAL      # at most 12 targets
+    assert lib.uly_create(ctypes.byref(h), -1, 4, 0) == _lib.E_INVAL
+    assert lib.uly_create(None, -1, 4, 12) == _lib.E_INVAL
+    assert lib.uly_destroy(None) == _lib.OK
+
+
+def test_scatter_valid_group_reaches_launch(lib, ctx4):
+    shape = (1, 16, 8, 128)
+    t_shape = (1, 64, 2, 128)
+    for i, tag in enumerate("qkv"):
+        assert register(lib, ctx4, tag, _lib.MODE_SCATTER, t_shape, BASE + (10 + i) * 64 * MiB) == _lib.OK
+    q, k, v = (T(BASE + i * 64 * MiB, shape) for i in range(3))
+    assert scatter(lib, ctx4, q, k, v) == _lib.E_UNSUPPORTED   # all checks passed, would launch
+
+
+def test_divisibility_checked_before_launch(lib, ctx4):
+    # heads 6 not divisible by P = 4
+    st = scatter(lib, ctx4, q=T(BASE, (1, 16, 6, 128)), tags=("q", None, None), outs=(BASE + 64 * MiB, None, None))
+    assert st == _lib.E_INVAL and b"divisible" in lib.uly_last_error()
+    # gathered sequence 18 not divisible by P = 4
+    o = T(BASE, (1, 18, 2, 128))
+    st = lib.ulysses_gather_out(ctx4.h, ctypes.byref(o), None, BASE + 64 * MiB, None)
+    assert st == _lib.E_INVAL and b"divisible" in lib.uly_last_error()
+
+
+def test_group_rejected_as_a_whole(lib, ctx4):
+    """A bad V leaves nothing launched for Q/K (no protocol mixing)."""
+    shape = (1, 16, 8, 128)
+    outs = (BASE + 10 * 64 * MiB, BASE + 11 * 64 * MiB, BASE + 12 * 64 * MiB)
+    bad_v = T(BASE + 2 * 64 * MiB, (1, 16, 8, 128), dtype=_lib.F16)
+    before = _stats(lib, ctx4)
+    st = scatter(lib, ctx4, T(BASE, shape), T(BASE + 64 * MiB, shape), bad_v, outs=outs)
+    assert st == _lib.E_DTYPE
+    assert _stats(lib, ctx4)["launches"] == before["launches"]
+    bad_v = T(BASE + 2 * 64 * MiB, (1, 17, 8, 128))                   # S_l differs
+    assert scatter(lib, ctx4, T(BASE, shape), T(BASE + 64 * MiB, shape), bad_v, outs=outs) == _lib.E_INVAL
+
+
+def _stats(lib, c):
+    s = _lib.UlyStats()
+    assert lib.uly_get_stats(c.h, ctypes.byref(s)) == _lib.OK
+    return {f: getattr(s, f) for f, _ in s._fields_}
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda t: setattr(t, "data", BASE + 8), _lib.E_INVAL),                   # misaligned
+    (lambda t: setattr(t, "data", 0), _lib.E_INVAL),                          # null
+    (lambda t: t.stride.__setitem__(3, 2), _lib.E_INVAL),                     # head dim not contiguous
+    (lambda t: t.shape.__setitem__(3, 36), _lib.E_INVAL),                     # D*2 % 16 != 0
+    (lambda t: setattr(t, "dtype", 7), _lib.E_DTYPE),
+    (lambda t: setattr(t, "reserved", 1), _lib.E_INVAL),
+    (lambda t: t.stride.__setitem__(1, 8 * 128 + 4), _lib.E_INVAL),           # row pitch not 16-byte
+    (lambda t: t.stride.__setitem__(2, 136), _lib.E_INVAL),                   # heads not packed
+])
+def test_operand_rejections(lib, ctx4, mutate, code):
+    t = T(BASE, (1, 16, 8, 128))
+    mutate(t)
+    assert scatter(lib, ctx4, q=t, tags=("q", None, None), outs=(BASE + 64 * MiB, None, None)) == code
+
+
+def test_overlap_rejected(lib, ctx4):
+    t = T(BASE, (1, 16, 8, 128))
+    assert scatter(lib, ctx4, q=t, tags=("q", None, None), outs=(BASE + 4096, None, None)) == _lib.E_OVERLAP
+    # two members writing the same destination
+    t2 = T(BASE + 64 * MiB, (1, 16, 8, 128))
+    st = scatter(lib, ctx4, q=t, k=t2, tags=("q", "k", None), outs=(BASE + 128 * MiB, BASE + 128 * MiB, None))
+    assert st == _lib.E_OVERLAP
+
+
+def test_fused_qkv_strided_source_accepted(lib, ctx4):
+    """V taken from a fused [B, S_l, 3, H, D] projection: stride[1] = 3*H*D, offset 2*H*D."""
+    B, S, H, D = 1, 16, 8, 128
+    rank = B * S * 3 * H * D
+    v = T(BASE + 2 * H * D * 2, (B, S, H, D), stride=(S * 3 * H * D, 3 * H * D, D, 1), rank_stride=rank)
+    assert scatter(lib, ctx4, v=v, tags=(None, None, "v"), outs=(None, None, BASE + 64 * MiB)) == _lib.E_UNSUPPORTED
+
+
+def test_target_cache_policy(lib):
+    c = Ctx(lib, 2, max_targets=12)
+    try:
+        for i in range(12):
+            assert register(lib, c, "t%d" % i, _lib.MODE_SCATTER, (1, 8, 4, 64), BASE + i * MiB) == _lib.OK
+        # a 13th key is refused (no eviction)
+        assert register(lib, c, "t12", _lib.MODE_SCATTER, (1, 8, 4, 64), BASE + 12 * MiB) == _lib.E_CACHE_FULL
+        n = ctypes.c_int()
+        lib.uly_target_count(c.h, ctypes.byref(n))
+        assert n.value == 12
+        # lookups return the registered pointer, stable across calls
+        for step in range(20):
+            p = ctypes.c_void_p()
+            assert lib.uly_target_lookup(c.h, b"t3", _lib.MODE_SCATTER, _lib.BF16, _lib.int64_array((1, 8, 4, 64)),
+                                         ctypes.byref(p)) == _lib.OK
+            assert p.value == BASE + 3 * MiB
+        # every key component matters: mode, dtype and shape
+        p = ctypes.c_void_p()
+        for mode, dtype, shape in [(_lib.MODE_GATHER, _lib.BF16, (1, 8, 4, 64)),
+                                   (_lib.MODE_SCATTER, _lib.F16, (1, 8, 4, 64)),
+                                   (_lib.MODE_SCATTER, _lib.BF16, (1, 8, 4, 128))]:
+            assert lib.uly_target_lookup(c.h, b"t3", mode, dtype, _lib.int64_array(shape),
+                                         ctypes.byref(p)) == _lib.E_NOT_FOUND
+        assert _stats(lib, c)["registrations"] == 12
+    finally:
+        c.close()
+
+
+def test_target_register_rejections(lib, ctx4):
+    shp = (1, 8, 4, 64)
+    assert register(lib, ctx4, "a", _lib.MODE_SCATTER, shp, BASE + 8) == _lib.E_INVAL          # misaligned
+    assert register(lib, ctx4, "a", _lib.MODE_SCATTER, shp, BASE, nbytes=100) == _lib.E_INVAL  # too small
+    assert register(lib, ctx4, "x" * 64, _lib.MODE_SCATTER, shp, BASE) == _lib.E_INVAL        # tag too long
+    assert register(lib, ctx4, "a", 5, shp, BASE) == _lib.E_INVAL
+    assert register(lib, ctx4, "a", _lib.MODE_SCATTER, shp, BASE, dtype=9) == _lib.E_DTYPE
+    assert register(lib, ctx4, "a", _lib.MODE_SCATTER, shp, BASE) == _lib.OK
+    assert register(lib, ctx4, "a", _lib.MODE_SCATTER, shp, BASE + MiB) == _lib.E_INVAL       # duplicate key
+
+
+def test_missing_and_mistyped_targets(lib, ctx4):
+    q = T(BASE, (1, 16, 8, 128))
+    assert scatter(lib, ctx4, q=q, tags=("q", None, None)) == _lib.E_NOT_FOUND
+    # registered as fp16, called with bf16: a dtype error, not a miss
+    assert register(lib, ctx4, "q", _lib.MODE_SCATTER, (1, 64, 2, 128), BASE + 64 * MiB, dtype=_lib.F16) == _lib.OK
+    assert scatter(lib, ctx4, q=q, tags=("q", None, None)) == _lib.E_DTYPE
+
+
+def _fused(lib, c, q, k, w=(BASE + 200 * MiB, BASE + 201 * MiB), eps=1e-6, rows=64,
+           tabs=(BASE + 300 * MiB, BASE + 310 * MiB), outs=(BASE + 100 * MiB, BASE + 120 * MiB)):
+    args = [ctypes.byref(x) if x is not None else None for x in (q, k)]
+    return lib.fused_qk_norm_rope_scatter(c.h, *args, w[0], w[1], eps, tabs[0], tabs[1], rows,
+                                          _lib.tags_array(("q", "k")), _lib.ptr_array(outs), None)
+
+
+def test_fused_rejections(lib, ctx4):
+    q, k = T(BASE, (1, 16, 8, 128)), T(BASE + 64 * MiB, (1, 16, 8, 128))
+    assert _fused(lib, ctx4, q, k) == _lib.E_UNSUPPORTED                      # valid: would launch
+    assert _fused(lib, ctx4, q, k, rows=63) == _lib.E_INVAL                   # positions reach 64
+    assert _fused(lib, ctx4, q, k, eps=0.0) == _lib.E_INVAL
+    assert _fused(lib, ctx4, q, k, eps=float("nan")) == _lib.E_INVAL
+    assert _fused(lib, ctx4, q, k, w=(0, BASE)) == _lib.E_INVAL
+    assert _fused(lib, ctx4, q, k, tabs=(BASE + 8, BASE)) == _lib.E_INVAL
+    assert _fused(lib, ctx4, None, None) == _lib.E_INVAL
+    k96 = T(BASE + 64 * MiB, (1, 16, 8, 96))
+    assert _fused(lib, ctx4, q, k96) == _lib.E_INVAL                          # D differs
+    q96 = T(BASE, (1, 16, 8, 96))
+    assert _fused(lib, ctx4, q96, None) == _lib.E_UNSUPPORTED and b"head dim" in lib.uly_last_error()
+    # GQA: Q and K may differ in heads
+    k2 = T(BASE + 64 * MiB, (1, 16, 4, 128))
+    assert _fused(lib, ctx4, q, k2) == _lib.E_UNSUPPORTED and b"host-only" in lib.uly_last_error()
+
+
+def test_fail_stop_after_launch_failure(lib):
+    c = Ctx(lib, 2)
+    try:
+        q = T(BASE, (1, 8, 4, 64))
+        assert lib.uly_debug_fail_launch(c.h, 0) == _lib.OK
+        st = scatter(lib, c, q=q, tags=("q", None, None), outs=(BASE + 64 * MiB, None, None))
+        assert st == _lib.E_HIP
+        # the context is poisoned: every later call refuses, even valid ones
+        assert scatter(lib, c, q=q, tags=("q", None, None), outs=(BASE + 64 * MiB, None, None)) == _lib.E_BROKEN
+        assert register(lib, c, "z", _lib.MODE_SCATTER, (1, 16, 2, 64), BASE) == _lib.E_BROKEN
+        assert lib.uly_wait(c.h, None) == _lib.E_BROKEN
+    finally:
+        assert lib.uly_destroy(c.h) == _lib.OK      # destroy is still allowed
+
+
+def test_argument_errors_leave_context_usable(lib, ctx4):
+    q = T(BASE, (1, 16, 6, 128))
+    assert scatter(lib, ctx4, q=q, tags=("q", None, None), outs=(BASE + 64 * MiB, None, None)) == _lib.E_INVAL
+    q = T(BASE, (1, 16, 8, 128))
+    assert scatter(lib, ctx4, q=q, tags=("q", None, None), outs=(BASE + 64 * MiB, None, None)) == _lib.E_UNSUPPORTED
+
+
+def test_pad_and_spatial_rejections(lib, ctx4):
+    # P*S_l must cover S
+    assert lib.uly_seq_pad_shard(ctx4.h, BASE, _lib.BF16, 1, 100, 64, 24, BASE + 64 * MiB, None) == _lib.E_INVAL
+    assert lib.uly_seq_pad_shard(ctx4.h, BASE, _lib.BF16, 1, 100, 64, 25, BASE + 64 * MiB, None) == _lib.E_UNSUPPORTED
+    assert lib.uly_seq_pad_shard(ctx4.h, BASE, _lib.BF16, 1, 100, 12, 25, BASE + 64 * MiB, None) == _lib.E_INVAL
+    assert lib.uly_seq_pad_shard(ctx4.h, BASE, _lib.BF16, 1, 100, 64, 25, BASE + 4096, None) == _lib.E_OVERLAP
+    # spatial: W*2 multiple of 16, height >= P
+    assert lib.uly_spatial_split_halo(ctx4.h, BASE, _lib.BF16, 336, 90, 160, 1, BASE + 64 * MiB, None) == _lib.E_UNSUPPORTED
+    assert lib.uly_spatial_split_halo(ctx4.h, BASE, _lib.BF16, 336, 90, 150, 1, BASE + 64 * MiB, None) == _lib.E_INVAL
+    assert lib.uly_spatial_split_halo(ctx4.h, BASE, _lib.BF16, 336, 3, 160, 1, BASE + 64 * MiB, None) == _lib.E_INVAL
+
+
+def test_fastdiv_exhaustive_edges(tmp_path):
+    """The kernels' division helper against integer division (host compiler)."""
+    src = tmp_path / "t.cpp"
+    src.write_text(r'''
+#include "fastdiv.h"
+#include <cstdio>
+#include <random>
+int main() {
+    std::mt19937_64 rng(1);
+    const uint32_t ds[] = {1, 2, 3, 5, 6, 7, 24, 40, 48, 96, 128, 160, 200, 4096, 18944, 75600, 75776,
+                           65535, 65537, 0x7fffffffu, 0x80000000u, 0x80000001u, 0xfffffffeu, 0xffffffffu};
+    long bad = 0;
+    for (uint32_t d : ds) {
+        uly::FastDiv f = uly::FastDiv::make(d);
+        const uint32_t edge[] = {0u, 1u, d - 1, d, d + 1, 2 * d - 1, 0x7fffffffu, 0x80000000u, 0xfffffffeu, 0xffffffffu};
+        for (uint32_t n : edge) { uint32_t q, r; f.divmod(n, q, r); bad += (q != n / d) || (r != n % d); }
+        for (int i = 0; i < 200000; ++i) { uint32_t n = uint32_t(rng()); uint32_t q, r; f.divmod(n, q, r);
+                                           bad += (q != n / d) || (r != n % d); }
+    }
+    for (int i = 0; i < 2000; ++i) {
+        uint32_t d = uint32_t(rng()) >> (rng() % 32); if (!d) d = 1;
+        uly::FastDiv f = uly::FastDiv::make(d);
+        for (int j = 0; j < 2000; ++j) { uint32_t n = uint32_t(rng()); bad += f.div(n) != n / d; }
+    }
+    printf("%ld\n", bad);
+    return bad != 0;
+}
+''')
+    exe = tmp_path / "t"
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "sequence_attention_ulysses_amd", "csrc"),
+                           str(src), "-o", str(exe)])
+    assert subprocess.check_output([str(exe)]).decode().strip() == "0"
+
+
+def test_library_rope_tables_match_oracle(orc):
+    from sequence_attention_ulysses_amd import rope_table_1d, rope_table_3d
+    c, s = rope_table_1d(4096 + 7, 128, real_rows=4096)
+    oc, os_ = orc.rope_table_1d(4096 + 7, 128, real_rows=4096)
+    # both evaluate in double and round once to fp32; allow one fp32 ulp for libm differences
+    np.testing.assert_allclose(c.numpy(), oc, rtol=0, atol=6e-8)
+    np.testing.assert_allclose(s.numpy(), os_, rtol=0, atol=6e-8)
+    c3, s3 = rope_table_3d(2 * 3600 + 100, 128, 60, 60, real_rows=2 * 3600 + 50)
+    oc3, os3 = orc.rope_table_3d(2 * 3600 + 100, 128, 60, 60, real_rows=2 * 3600 + 50)
+    np.testing.assert_allclose(c3.numpy(), oc3, rtol=0, atol=6e-8)
+    np.testing.assert_allclose(s3.numpy(), os3, rtol=0, atol=6e-8)
+
+
+def test_python_binding_host_only():
+    """The binding marshals arguments only; a host-only context exposes the cache."""
+    import warnings
+
+    from sequence_attention_ulysses_amd import UlyssesContext
+    c = UlyssesContext(4, device=None)
+    assert c.target_count() == 0
+    c.close()
+    c2 = UlyssesContext(2, device=None)
+    with warnings.catch_warnings(record=True) as w:
+        warnings.simplefilter("always")
+        c2.__del__()
+        assert any(issubclass(x.category, ResourceWarning) for x in w)
+    c2.close()
