@@ -39,16 +39,26 @@ def to_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def assert_close16(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str):
-    """max-abs <= tolerance and within one 16-bit ulp of the oracle value."""
+    """max-abs <= tolerance, and every element within one 16-bit ulp of the oracle
+    value plus the fp32 evaluation error.
+
+    The kernel evaluates in fp32 and rounds once.  Rounding costs at most half
+    an ulp of y; the fp32 evaluation of y_2j = n_2j c - n_2j+1 s (and its twin)
+    errs by a few fp32 ulps of the rotated pair's magnitude |(n_2j, n_2j+1)|,
+    which can exceed a 16-bit ulp of y itself when the two products cancel.
+    The slack is 2^-18 of the pair magnitude (~64 fp32 ulps)."""
     g = got.detach().cpu().double().numpy()
     assert g.shape == ref.shape, (g.shape, ref.shape)
     err = np.abs(g - ref)
     mag = np.abs(ref)
     ulp = np.exp2(np.maximum(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - MANT[dtype], SUB[dtype]))
     ulp = np.where(mag > 0, ulp, 2.0 ** SUB[dtype])
-    over_ulp = err > ulp * (1 + 1e-9)
-    assert not over_ulp.any(), "%s: %d elements more than one ulp from the oracle (max err %g)" % (
-        what, int(over_ulp.sum()), float(err.max()))
+    pair = np.sqrt(ref[..., 0::2] ** 2 + ref[..., 1::2] ** 2)
+    pair = np.repeat(pair, 2, axis=-1)
+    bound = ulp + pair * 2.0 ** -18
+    over_ulp = err > bound
+    assert not over_ulp.any(), "%s: %d elements beyond one ulp + fp32 slack (worst excess %g at |y|=%g)" % (
+        what, int(over_ulp.sum()), float((err - bound).max()), float(mag[over_ulp][0]))
     over_tol = err > TOL[dtype]
     # a one-ulp flip above |y| = 8 (bf16) exceeds the tolerance by construction: classify, do not loosen
     unexplained = over_tol & ~(ulp > TOL[dtype])
