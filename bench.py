@@ -3,18 +3,22 @@
 
 A step is the whole hot path over one batch of synthetic inputs already
 resident in HBM:
-  1. V scattered from the fused QKV projection on the library's comm stream,
-  2. Q/K RMSNorm + RoPE fused into their scatter on the caller's stream,
-  3. the grouped wait (the caller stream joins the comm stream),
-  4. the attention output gathered back from head-sharded to sequence-sharded.
+  1. Q/K RMSNorm + RoPE fused into their scatter, with V scattered in the
+     same launch (one grid moves all of Q, K and V to head-sharded targets),
+  2. the grouped wait,
+  3. the attention output gathered back from head-sharded to
+     sequence-sharded.
+The two-stream form of step 1 (V on the library's comm stream overlapping
+the fused Q/K kernel on the caller's stream) is timed alongside and reported
+under "two_stream".
 
 Workload: the video-DiT block with P=4 emulated ranks, B=1, S_local=4096
-(S=16384), H=24, D=128, bf16.  The metric is algorithmic bytes per step (each
-input element read once and each output element written once: 805,306,368 B)
-over wall time, in GB/s, and as a fraction of the 8 TB/s HBM peak.
+(S=16384), H=24, D=128, bf16, V strided from the fused QKV projection.  The
+metric is algorithmic bytes per step (each input element read once and each
+output element written once: 805,306,368 B) over wall time, in GB/s, and as
+a fraction of the 8 TB/s HBM peak.
 
-Prints one JSON line (rank 0).  --gpus N with N > 1 exits: this build runs on
-one GPU.
+Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
 """
 from __future__ import annotations
 
@@ -55,8 +59,9 @@ def traffic_from_profiles(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(args, inputs):
-    """The CPU oracle, as it stands, on one full step of the same workload."""
+def cpu_baseline(args, inputs, min_seconds: float = 10.0):
+    """The CPU oracle, as it stands, on whole steps of the same workload,
+    repeated until about `min_seconds` of CPU work."""
     import numpy as np
 
     from oracle import oracle
@@ -65,17 +70,39 @@ def cpu_baseline(args, inputs):
     qkv, w_q, w_k, o = (synth.bits(t) for t in inputs)
     w = synth.VIDEO_DIT
     cos, sin = oracle.rope_table_1d(w.S, w.D, theta=w.theta)
-    t0 = time.perf_counter()
-    yv = oracle.scatter(np.ascontiguousarray(qkv[:, :, :, 2]))
-    yq = oracle.fused_norm_rope_scatter(np.ascontiguousarray(qkv[:, :, :, 0]), "bf16", w_q, w.eps, cos, sin)
-    yk = oracle.fused_norm_rope_scatter(np.ascontiguousarray(qkv[:, :, :, 1]), "bf16", w_k, w.eps, cos, sin)
-    z = oracle.gather(o)
-    dt = time.perf_counter() - t0
-    del yv, yq, yk, z
-    return {"value": round(args.bytes_per_step / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "one full step of the workload (V scatter, fused Q/K norm+RoPE scatter, output gather; "
-                      "%d algorithmic bytes) in %.2f s, single-threaded C oracle in double" %
-                      (args.bytes_per_step, dt)}
+    q_src, k_src, v_src = (np.ascontiguousarray(qkv[:, :, :, c]) for c in range(3))
+    steps, dt = 0, 0.0
+    while dt < min_seconds:
+        t0 = time.perf_counter()
+        yv = oracle.scatter(v_src)
+        yq = oracle.fused_norm_rope_scatter(q_src, "bf16", w_q, w.eps, cos, sin)
+        yk = oracle.fused_norm_rope_scatter(k_src, "bf16", w_k, w.eps, cos, sin)
+        z = oracle.gather(o)
+        dt += time.perf_counter() - t0
+        steps += 1
+        del yv, yq, yk, z
+    return {"value": round(steps * args.bytes_per_step / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d full steps of the workload (V scatter, Q/K norm+RoPE scatter, output gather; "
+                      "%d algorithmic bytes each) in %.1f s, single-threaded C oracle in double"
+                      % (steps, args.bytes_per_step, dt)}
+
+
+def calibrate_copy(args, torch, UlyssesContext):
+    """A plain copy of a known size through the library's relayout kernel
+    (one rank, so the map is the identity): the reference that scales the
+    FETCH_SIZE / WRITE_SIZE counters of the step's kernels."""
+    nbytes = args.calibrate_copy << 20
+    rows = nbytes // (128 * 128 * 2)
+    src = torch.ones((1, 1, rows, 128, 128), dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    with UlyssesContext(1, device=0) as ctx:
+        for _ in range(args.warmup + args.steps):
+            ctx.scatter_qkv(q=src, out=(dst, None, None))
+            ctx.wait()
+        torch.cuda.synchronize()
+    print(json.dumps({"calibration": "relayout_kernel plain copy", "bytes_read_per_launch": nbytes,
+                      "bytes_written_per_launch": nbytes, "launches": args.warmup + args.steps}), flush=True)
 
 
 def main():
@@ -87,6 +114,11 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time each step after a 1 GiB scrub of the caches (event-timed, reported apart)")
     ap.add_argument("--no-profile", action="store_true", help="do not bracket launches with timing events")
+    ap.add_argument("--no-two-stream", action="store_true",
+                    help="skip the two-stream comparison (profiling runs then hold only the headline step)")
+    ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
+                    help="instead of the step, run a plain device copy of MIB MiB (the library's relayout with "
+                         "one rank) to calibrate HBM byte counters against a known size")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -97,6 +129,10 @@ def main():
     import torch
 
     from sequence_attention_ulysses_amd import UlyssesContext, rope_table_1d, synth
+
+    if args.calibrate_copy:
+        calibrate_copy(args, torch, UlyssesContext)
+        return
 
     w = synth.VIDEO_DIT
     P, B, S_l, H, D = w.P, w.B, w.S_l, w.Hq, w.D
@@ -119,30 +155,41 @@ def main():
     ctx = UlyssesContext(P, device=0)
 
     def step():
-        ctx.scatter_qkv(v=v_in)
+        ctx.fused_qk_norm_rope_scatter(q_in, k_in, g_wq, g_wk, g_cos, g_sin, eps=w.eps, v=v_in)
+        ctx.wait()
+        ctx.gather_out(g_o)
+
+    def step_two_stream():
+        ctx.scatter_qkv(v=v_in, tags=(None, None, "v2"))
         ctx.fused_qk_norm_rope_scatter(q_in, k_in, g_wq, g_wk, g_cos, g_sin, eps=w.eps)
         ctx.wait()
         ctx.gather_out(g_o)
 
+    def timed(fn, steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
     for _ in range(args.warmup):
         step()
+        if not args.no_two_stream:
+            step_two_stream()
     torch.cuda.synchronize()
     if not args.no_profile:
-        ctx.profile(True)
+        # time only the dominant kernel: every event pair adds latency between kernels
+        ctx.profile(True, kinds=["norm_rope"])
         ctx.profile_reset()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall = timed(step, args.steps)
     ms_per_step = wall * 1e3 / args.steps
     value = args.bytes_per_step / (wall / args.steps) / 1e9
 
     kernels = {}
     roofline = None
     if not args.no_profile:
-        per_launch_bytes = {"norm_rope": 2 * 2 * n_tensor, "scatter": 2 * n_tensor, "gather": 2 * n_tensor}
+        per_launch_bytes = {"norm_rope": 6 * n_tensor}
         for kind, nbytes in per_launch_bytes.items():
             ms, n = ctx.profile_read(kind)
             if n:
@@ -150,13 +197,21 @@ def main():
                 kernels[kind] = {"launches": n, "avg_us": round(avg_us, 2), "bytes_per_launch": nbytes,
                                  "GB_s": round(nbytes / (avg_us * 1e-6) / 1e9, 1)}
         ctx.profile(False)
+        ctx.profile_reset()
         dom = kernels.get("norm_rope")
         if dom:
             achieved = dom["GB_s"]
             roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(w.name),
-                        "kernel": "norm_rope_kernel<16,bf16> (fused Q/K RMSNorm+RoPE scatter)",
+                        "kernel": "norm_rope_kernel<16,bf16> (Q/K RMSNorm+RoPE scatter with V in the same grid)",
                         "algorithmic_bytes_per_launch": dom["bytes_per_launch"], "avg_us": dom["avg_us"]}
+
+    # the two-stream form of the same step, timed the same way (no events)
+    two_stream = None
+    if not args.no_two_stream:
+        wall2 = timed(step_two_stream, args.steps)
+        two_stream = {"ms_per_step": round(wall2 * 1e3 / args.steps, 5),
+                      "GB_s": round(args.bytes_per_step / (wall2 / args.steps) / 1e9, 2)}
 
     cold = None
     if args.cold:
@@ -201,6 +256,7 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": roofline,
         "kernels": kernels,
+        "two_stream": two_stream,
         "cpu_baseline": cpu,
     }
     if cold:

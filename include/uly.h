@@ -176,19 +176,22 @@ uly_status ulysses_scatter_qkv(uly_ctx *ctx, const uly_tensor *q, const uly_tens
  *     c = cos_tab[g][j], s = sin_tab[g][j], g = r*S_l + s   (fp32)
  * rounded once to the operand dtype (round to nearest even) and stored at
  * Y[h / Hl][b][g][h % Hl][:] — no intermediate tensor.
- * q, k: operands (either may be NULL), same B, S_l, D, dtype; H % P == 0.
+ * q, k: operands normalised and rotated (either may be NULL); v: optional
+ *     operand scattered unchanged in the same launch, as the fused producer
+ *     of [QN "Description"] stores every destination's q, k and v band.
+ *     All members share B, S_l, D and dtype; H % P == 0 for each.
  * w_q, w_k: [D] weights in the operand dtype (required for each non-NULL
- *     operand).  eps: > 0 (1e-6 in [QN]).
+ *     q / k).  eps: > 0 (1e-6 in [QN]).
  * cos_tab, sin_tab: device fp32 [table_rows][D/2], row g = global position;
  *     table_rows >= P*S_l.  D must be even and D*2 a multiple of 16 with
  *     D*2/16 in {4, 8, 16, 32} lanes per row (D = 32, 64, 128, 256).
- * tags / outs: as in ulysses_scatter_qkv (members 0 = q, 1 = k).
+ * tags / outs: as in ulysses_scatter_qkv (members 0 = q, 1 = k, 2 = v).
  * caller: the kernel runs on this stream (the compute stream). */
 uly_status fused_qk_norm_rope_scatter(uly_ctx *ctx, const uly_tensor *q, const uly_tensor *k,
-                                      const void *w_q, const void *w_k, float eps,
-                                      const float *cos_tab, const float *sin_tab,
-                                      int64_t table_rows, const char *const tags[2],
-                                      void *const outs[2], hipStream_t caller);
+                                      const uly_tensor *v, const void *w_q, const void *w_k,
+                                      float eps, const float *cos_tab, const float *sin_tab,
+                                      int64_t table_rows, const char *const tags[3],
+                                      void *const outs[3], hipStream_t caller);
 
 /* Grouped completion handshake ([P27 "Changes Made": one grouped handshake
  * for the tagged Q/K/V transfers]): make `consumer` wait, without any
@@ -267,11 +270,13 @@ typedef enum {
     ULY_K_COUNT = 5
 } uly_kernel_kind;
 
-/* When on, every launch is bracketed by HIP events on the stream it runs
- * on; uly_profile_read waits for those events and returns the summed
- * kernel time (ms) and the number of launches of `kind` since the last
- * reset. */
-uly_status uly_profile_enable(uly_ctx *ctx, int on);
+/* kind_mask bit k (1 << uly_kernel_kind) brackets every launch of kind k
+ * with HIP events on the stream it runs on (0 turns timing off; each pair
+ * of events adds a little latency between kernels, so time only what is
+ * needed); uly_profile_read waits for those events and returns the summed
+ * kernel time (ms) and the number of timed launches of `kind` since the
+ * last reset. */
+uly_status uly_profile_enable(uly_ctx *ctx, int kind_mask);
 uly_status uly_profile_read(uly_ctx *ctx, int kind, double *total_ms, int64_t *launches);
 uly_status uly_profile_reset(uly_ctx *ctx);
 

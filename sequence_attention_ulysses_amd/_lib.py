@@ -133,7 +133,7 @@ def load() -> ctypes.CDLL:
         "uly_target_lookup": [vp, cp, i32, i32, P_I64, ctypes.POINTER(vp)],
         "uly_target_count": [vp, ctypes.POINTER(i32)],
         "ulysses_scatter_qkv": [vp, P_T, P_T, P_T, TAGS, OUTS, vp],
-        "fused_qk_norm_rope_scatter": [vp, P_T, P_T, vp, vp, f32, vp, vp, i64, TAGS, OUTS, vp],
+        "fused_qk_norm_rope_scatter": [vp, P_T, P_T, P_T, vp, vp, f32, vp, vp, i64, TAGS, OUTS, vp],
         "uly_wait": [vp, vp],
         "ulysses_gather_out": [vp, P_T, cp, vp, vp],
         "uly_seq_pad_shard": [vp, vp, i32, i64, i64, i64, i64, vp, vp],

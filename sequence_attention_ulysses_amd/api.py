@@ -199,16 +199,17 @@ class UlyssesContext:
                                             _stream_handle(stream)), "ulysses_scatter_qkv")
         return dests
 
-    def fused_qk_norm_rope_scatter(self, q, k, w_q, w_k, cos, sin, eps: float = 1e-6, tags=("q", "k"),
-                                   out=None, stream=None):
+    def fused_qk_norm_rope_scatter(self, q, k, w_q, w_k, cos, sin, eps: float = 1e-6, v=None,
+                                   tags=("q", "k", "v"), out=None, stream=None):
         """Q/K RMSNorm + interleaved RoPE + scatter in one kernel on the caller's stream.
 
+        v (optional) is scattered unchanged in the same launch.
         cos/sin: device fp32 [rows >= P*S_l, D/2] tables indexed by global position.
-        Returns the destination tensors [P, B, P*S_l, H/P, D] (None for an absent member).
+        Returns the destination tensors [P, B, P*S_l, H/P, D] of (q, k, v) (None for absent members).
         """
         P = self.world_size
-        mem = (q, k)
-        self._on_device(q, k, w_q, w_k, cos, sin)
+        mem = (q, k, v)
+        self._on_device(q, k, v, w_q, w_k, cos, sin)
         descs, dests, ptrs = [], [], []
         for i, x in enumerate(mem):
             if x is None:
@@ -218,7 +219,8 @@ class UlyssesContext:
                 descs.append(describe(x)); dests.append(None); ptrs.append(None)
                 continue
             shape = (x.shape[1], x.shape[2] * P, x.shape[3] // P, x.shape[4])
-            d, explicit = self._dest(tags[i], _lib.MODE_SCATTER, x, shape, None if out is None else out[i])
+            o_i = None if out is None or i >= len(out) else out[i]
+            d, explicit = self._dest(tags[i], _lib.MODE_SCATTER, x, shape, o_i)
             descs.append(describe(x)); dests.append(d)
             ptrs.append(d.data_ptr() if explicit else None)
         for t in (cos, sin):
@@ -233,9 +235,10 @@ class UlyssesContext:
             if x is not None and w is not None and (w.dtype != x.dtype or not w.is_contiguous()
                                                     or w.numel() != x.shape[-1]):
                 raise ValueError("norm weights must be contiguous [D] tensors in the operand dtype")
-        for x in (q, k):
+        for x in (q, k, v):
             if x is not None and x.dim() == 5 and cos.shape[1] * 2 != x.shape[-1]:
                 raise ValueError("cos/sin tables must have D/2 columns")
+        tags = tuple(tags) + (None,) * (3 - len(tags))
         check(self._lib.fused_qk_norm_rope_scatter(self._h(), *args, wq, wk, float(eps), cos.data_ptr(),
                                                    sin.data_ptr(), cos.shape[0], _lib.tags_array(tags),
                                                    _lib.ptr_array(ptrs), _stream_handle(stream)),
@@ -348,8 +351,17 @@ class UlyssesContext:
         return out
 
     # -- measurement --------------------------------------------------------------
-    def profile(self, on: bool = True) -> None:
-        check(self._lib.uly_profile_enable(self._h(), int(bool(on))), "uly_profile_enable")
+    def profile(self, on: bool = True, kinds=None) -> None:
+        """Bracket launches with timing events: all kinds, or only `kinds` (names of KERNEL_KINDS)."""
+        if not on:
+            mask = 0
+        elif kinds is None:
+            mask = (1 << len(_lib.KERNEL_KINDS)) - 1
+        else:
+            mask = 0
+            for k in kinds:
+                mask |= 1 << _lib.KERNEL_KINDS[k]
+        check(self._lib.uly_profile_enable(self._h(), mask), "uly_profile_enable")
 
     def profile_read(self, kind: str):
         """(summed kernel ms, launches) of one kernel kind since the last reset."""

@@ -40,8 +40,9 @@ struct CopyBatch {
 
 // ---------------------------------------------------------------------------
 // Fused RMSNorm + RoPE + scatter.  Rows are (r, b, s, hh) in source order,
-// hh in [0, H0 + H1): hh < H0 reads operand 0 (Q), the rest operand 1 (K),
-// so one token's Q and K heads are consecutive rows and share one table row.
+// hh in [0, H0 + H1 + H2): hh < H0 reads operand 0 (Q), hh < H0 + H1
+// operand 1 (K), the rest operand 2 (V, copied unchanged), so the rows of
+// one token share one table row.
 // ---------------------------------------------------------------------------
 struct NormRopeOperand {
     const uint16_t *src;
@@ -55,17 +56,17 @@ struct NormRopeOperand {
 };
 
 struct NormRopeArgs {
-    NormRopeOperand op[2];
+    NormRopeOperand op[3];
     const float *cos_tab;
     const float *sin_tab;
-    FastDiv rpt;        // rows per token = H0 + H1
+    FastDiv rpt;        // rows per token = H0 + H1 + H2
     FastDiv sl;         // S_l
     FastDiv bdiv;       // B
     uint32_t H0;        // rows of operand 0 per token (0 when absent)
-    uint32_t rows;      // P*B*S_l*(H0+H1)
+    uint32_t H01;       // H0 + H1
+    uint32_t tokens;    // P*B*S_l
     uint32_t S_l;
     uint32_t D;
-    uint32_t rows_per_block;
     float eps;
     float inv_D;
 };
@@ -104,13 +105,26 @@ struct RowMapArgs {
 // Launch wrappers (uly_kernels.hip).  They only enqueue; the caller checks
 // hipGetLastError().
 void launch_relayout(const CopyBatch &b, hipStream_t stream);
-void launch_norm_rope(const NormRopeArgs &a, int lanes, int dtype, uint32_t blocks, hipStream_t stream);
+void launch_norm_rope(const NormRopeArgs &a, int lanes, int dtype, bool uniform, bool tile, uint32_t blocks,
+                      hipStream_t stream);
 void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
 
-constexpr int kThreads = 256;
-constexpr int kCopyUnroll = 4;                           // 16-byte vectors per thread
+#ifndef ULY_THREADS
+#define ULY_THREADS 256
+#endif
+#ifndef ULY_COPY_UNROLL
+#define ULY_COPY_UNROLL 4
+#endif
+#ifndef ULY_ROPE_TOKENS
+#define ULY_ROPE_TOKENS 4
+#endif
+#ifndef ULY_ROPE_THREADS
+#define ULY_ROPE_THREADS 512
+#endif
+constexpr int kThreads = ULY_THREADS;
+constexpr int kCopyUnroll = ULY_COPY_UNROLL;             // 16-byte vectors per thread
 constexpr uint32_t kCopyVecsPerBlock = kThreads * kCopyUnroll;
-constexpr int kRopeUnroll = 4;                           // rows in flight per lane group
-constexpr int kRopeItersPerBlock = 2;                    // unrolled passes per block
+constexpr int kRopeTokens = ULY_ROPE_TOKENS;            // tokens per block (rows in flight per group)
+constexpr int kRopeThreads = ULY_ROPE_THREADS;          // threads per block of the fused kernel
 
 }  // namespace uly

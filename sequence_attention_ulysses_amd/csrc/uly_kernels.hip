@@ -25,12 +25,45 @@
 namespace uly {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+
+// All operands live in device (global) memory: the explicit address space
+// keeps the accesses global_load/store instead of flat ones.  Operand data
+// streams through exactly once, so its 16-byte accesses are non-temporal
+// (they do not displace lines that are reused); building with
+// ULY_TEMPORAL_STREAMS turns that off.
 __device__ __forceinline__ uint4 load16(const void *p) {
-    return *reinterpret_cast<const uint4 *>(p);
+    const global_u32x4 *g = (const global_u32x4 *)p;
+#ifndef ULY_TEMPORAL_STREAMS
+    const u32x4 v = __builtin_nontemporal_load(g);
+#else
+    const u32x4 v = *g;
+#endif
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 __device__ __forceinline__ void store16(void *p, uint4 v) {
-    *reinterpret_cast<uint4 *>(p) = v;
+    global_u32x4 *g = (global_u32x4 *)p;
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+#ifndef ULY_TEMPORAL_STREAMS
+    __builtin_nontemporal_store(w, g);
+#else
+    *g = w;
+#endif
+}
+
+// Data every block re-reads (norm weights): ordinary cached load.
+__device__ __forceinline__ uint4 load16_cached(const void *p) {
+    const u32x4 v = *(const global_u32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Table rows are re-read by every head of a token: ordinary cached loads.
+__device__ __forceinline__ float4 load_table4(const float *p) {
+    const global_u32x4 *g = (const global_u32x4 *)p;
+    const u32x4 v = *g;
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 
 // ---------------------------------------------------------------------------
@@ -124,91 +157,140 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     }
 }
 
-template <int LANES, int DT>
-__global__ __launch_bounds__(kThreads) void norm_rope_kernel(NormRopeArgs a) {
-    constexpr int GROUPS = kThreads / LANES;
+template <class T>
+__device__ __forceinline__ T sel3(uint32_t i, T a, T b, T c) {
+    return i == 0 ? a : (i == 1 ? b : c);
+}
+
+// Work mapping.  A block owns a tile of kRopeTokens consecutive tokens
+// (source order r, b, s).  Its GROUPS lane groups split the R = H0+H1+H2
+// rows of a token: group gi owns the row slots hh = gi, gi + GROUPS, ...,
+// the same for every token, so the per-head part of the addressing is
+// computed once per slot, and the token part (r, b, s, g and the token
+// offsets) is the same for every lane of the block and lives in scalar
+// registers.
+//   UNI:  every operand's head count is a multiple of the groups per wave,
+//         so a wave's slots never straddle two operands: the operand of a
+//         slot is wave-uniform and every per-operand field is a scalar.
+//   TILE: S_l is a multiple of the tile, so a tile never crosses a rank or
+//         batch boundary: one decode per block, token t of the tile is
+//         s0 + t at global position g0 + t, and there is no partial tile.
+// Rows of operand 2 (V) ride in the same grid as plain 16-byte copies: the
+// whole Q/K/V scatter is one launch that shares HBM bandwidth without a
+// second kernel's ramp-up and tail.
+template <int LANES, int DT, bool UNI, bool TILE>
+__global__ __launch_bounds__(kRopeThreads) void norm_rope_kernel(NormRopeArgs a) {
+    constexpr int GROUPS = kRopeThreads / LANES;
+    constexpr int TU = kRopeTokens;
     const uint32_t lane = threadIdx.x % LANES;
     const uint32_t grp = threadIdx.x / LANES;
     const uint32_t half = a.D / 2;
+    const uint32_t R = a.rpt.d;
+    const uint32_t tk0 = blockIdx.x * TU;
+    const NormRopeOperand &o0 = a.op[0], &o1 = a.op[1], &o2 = a.op[2];
 
-    float w0[8], w1[8];
+    // TILE: the block's tokens, decoded once.
+    uint32_t r0 = 0, b0 = 0, s0 = 0, g0 = 0;
+    if (TILE) {
+        uint32_t rb;
+        a.sl.divmod(tk0, rb, s0);
+        a.bdiv.divmod(rb, r0, b0);
+        g0 = r0 * a.S_l + s0;
+    }
+
+    // Every lane of a group runs the same slot and token trips; tokens past
+    // the end (only without TILE) are computed on a clamped row and not
+    // stored, so every lane of a group takes part in every DPP exchange.
+    for (uint32_t hh = grp; hh < R; hh += GROUPS) {
+        // per-slot (per-head) part
+        const uint32_t hh_op = UNI ? __builtin_amdgcn_readfirstlane(hh) : hh;
+        const uint32_t oi = (hh_op >= a.H0 ? 1u : 0u) + (hh_op >= a.H01 ? 1u : 0u);
+        const uint32_t h = hh - sel3(oi, 0u, a.H0, a.H01);
+        uint32_t qd, j;
+        if (oi == 0) o0.hl.divmod(h, qd, j);
+        else if (oi == 1) o1.hl.divmod(h, qd, j);
+        else o2.hl.divmod(h, qd, j);
+        const int64_t s_rank = sel3(oi, o0.s_rank, o1.s_rank, o2.s_rank);
+        const int64_t s_b = sel3(oi, o0.s_b, o1.s_b, o2.s_b);
+        const int64_t s_s = sel3(oi, o0.s_s, o1.s_s, o2.s_s);
+        const int64_t d_b = sel3(oi, o0.d_b, o1.d_b, o2.d_b);
+        const int64_t d_g = sel3(oi, o0.d_g, o1.d_g, o2.d_g);
+        const uint16_t *src_h = sel3(oi, o0.src, o1.src, o2.src) +
+                                int64_t(h) * sel3(oi, o0.s_h, o1.s_h, o2.s_h) + lane * 8;
+        uint16_t *dst_h = sel3(oi, o0.dst, o1.dst, o2.dst) +
+                          int64_t(qd) * sel3(oi, o0.d_q, o1.d_q, o2.d_q) + int64_t(j) * a.D + lane * 8;
+        const bool rope = oi < 2;
+        float w[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w0[i] = w1[i] = 0.f;
-    if (a.op[0].w) unpack8<DT>(load16(a.op[0].w + lane * 8), w0);
-    if (a.op[1].w) unpack8<DT>(load16(a.op[1].w + lane * 8), w1);
+        for (int i = 0; i < 8; ++i) w[i] = 0.f;
+        if (rope) unpack8<DT>(load16_cached(sel3(oi, o0.w, o1.w, o2.w) + lane * 8), w);
 
-    const uint32_t row_begin = blockIdx.x * a.rows_per_block;
-    const uint32_t row_end = min(row_begin + a.rows_per_block, a.rows);
-
-    // The trip count is the same for every lane of the block; rows past
-    // row_end are computed on zeros and not stored, so every lane takes
-    // part in every DPP exchange.
-    for (uint32_t base = row_begin; base < row_end; base += GROUPS * kRopeUnroll) {
-        uint4 raw[kRopeUnroll];
-        float4 cs[kRopeUnroll], sn[kRopeUnroll];
-        uint16_t *dst[kRopeUnroll];
-        bool second[kRopeUnroll];
+        uint4 raw[TU];
+        float4 cs[TU], sn[TU];
+        int64_t doff[TU];
+        bool live[TU];
+        if (TILE) {
+            const uint16_t *src_t = src_h + (int64_t(r0) * s_rank + int64_t(b0) * s_b + int64_t(s0) * s_s);
+            const int64_t d0 = int64_t(b0) * d_b + int64_t(g0) * d_g;
 #pragma unroll
-        for (int k = 0; k < kRopeUnroll; ++k) {
-            const uint32_t row = base + grp + k * GROUPS;
-            raw[k] = make_uint4(0, 0, 0, 0);
-            cs[k] = make_float4(1.f, 1.f, 1.f, 1.f);
-            sn[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-            dst[k] = nullptr;
-            second[k] = false;
-            if (row < row_end) {
-                uint32_t tk, hh, rb, s, r, b;
-                a.rpt.divmod(row, tk, hh);
+            for (int t = 0; t < TU; ++t) {
+                live[t] = true;
+                raw[t] = load16(src_t + t * s_s);
+                doff[t] = d0 + t * d_g;
+            }
+#pragma unroll
+            for (int t = 0; t < TU; ++t) {
+                cs[t] = make_float4(1.f, 1.f, 1.f, 1.f);
+                sn[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (rope) {
+                    const size_t t_off = size_t(g0 + t) * half + lane * 4;
+                    cs[t] = load_table4(a.cos_tab + t_off);
+                    sn[t] = load_table4(a.sin_tab + t_off);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TU; ++t) {
+                live[t] = tk0 + t < a.tokens;      // uniform across the block
+                const uint32_t tk = live[t] ? tk0 + t : a.tokens - 1;
+                uint32_t rb, s, r, b;
                 a.sl.divmod(tk, rb, s);
                 a.bdiv.divmod(rb, r, b);
-                // Q or K row: select the operand's fields by value (both
-                // operands stay in scalar registers).
-                const bool k_op = hh >= a.H0;
-                const NormRopeOperand &o0 = a.op[0], &o1 = a.op[1];
-                const uint32_t h = hh - (k_op ? a.H0 : 0u);
                 const uint32_t g = r * a.S_l + s;
-                uint32_t qd, j;
-                if (k_op) o1.hl.divmod(h, qd, j); else o0.hl.divmod(h, qd, j);
-                const int64_t s_off = int64_t(r) * (k_op ? o1.s_rank : o0.s_rank) +
-                                      int64_t(b) * (k_op ? o1.s_b : o0.s_b) +
-                                      int64_t(s) * (k_op ? o1.s_s : o0.s_s) +
-                                      int64_t(h) * (k_op ? o1.s_h : o0.s_h) + lane * 8;
-                const int64_t d_off = int64_t(qd) * (k_op ? o1.d_q : o0.d_q) +
-                                      int64_t(b) * (k_op ? o1.d_b : o0.d_b) +
-                                      int64_t(g) * (k_op ? o1.d_g : o0.d_g) +
-                                      int64_t(j) * a.D + lane * 8;
-                const uint16_t *src = (k_op ? o1.src : o0.src) + s_off;
-                dst[k] = (k_op ? o1.dst : o0.dst) + d_off;
-                second[k] = k_op;
-                raw[k] = load16(src);
-                const size_t t_off = size_t(g) * half + lane * 4;
-                cs[k] = *reinterpret_cast<const float4 *>(a.cos_tab + t_off);
-                sn[k] = *reinterpret_cast<const float4 *>(a.sin_tab + t_off);
+                raw[t] = load16(src_h + (int64_t(r) * s_rank + int64_t(b) * s_b + int64_t(s) * s_s));
+                doff[t] = int64_t(b) * d_b + int64_t(g) * d_g;
+                cs[t] = make_float4(1.f, 1.f, 1.f, 1.f);
+                sn[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (rope) {
+                    const size_t t_off = size_t(g) * half + lane * 4;
+                    cs[t] = load_table4(a.cos_tab + t_off);
+                    sn[t] = load_table4(a.sin_tab + t_off);
+                }
             }
         }
 #pragma unroll
-        for (int k = 0; k < kRopeUnroll; ++k) {
+        for (int t = 0; t < TU; ++t) {
             float x[8];
-            unpack8<DT>(raw[k], x);
+            unpack8<DT>(raw[t], x);
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
             ss = row_sum<LANES>(ss);
-            const float inv = rsqrtf(fmaf(ss, a.inv_D, a.eps));
-            const float c[4] = {cs[k].x, cs[k].y, cs[k].z, cs[k].w};
-            const float sv[4] = {sn[k].x, sn[k].y, sn[k].z, sn[k].w};
+            // eps > 0 keeps the argument normal: the bare reciprocal square root suffices
+            const float inv = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_D, a.eps));
+            const float c[4] = {cs[t].x, cs[t].y, cs[t].z, cs[t].w};
+            const float sv[4] = {sn[t].x, sn[t].y, sn[t].z, sn[t].w};
             uint32_t out[4];
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const float wa = second[k] ? w1[2 * p] : w0[2 * p];
-                const float wb = second[k] ? w1[2 * p + 1] : w0[2 * p + 1];
-                const float n0 = x[2 * p] * inv * wa;
-                const float n1 = x[2 * p + 1] * inv * wb;
+                const float n0 = x[2 * p] * inv * w[2 * p];
+                const float n1 = x[2 * p + 1] * inv * w[2 * p + 1];
                 const float y0 = n0 * c[p] - n1 * sv[p];
                 const float y1 = n0 * sv[p] + n1 * c[p];
                 out[p] = pack2<DT>(y0, y1);
             }
-            if (dst[k]) store16(dst[k], make_uint4(out[0], out[1], out[2], out[3]));
+            const uint4 res = rope ? make_uint4(out[0], out[1], out[2], out[3]) : raw[t];  // V: unchanged
+            if (live[t]) store16(dst_h + doff[t], res);
         }
     }
 }
@@ -290,15 +372,29 @@ void launch_relayout(const CopyBatch &b, hipStream_t stream) {
     hipLaunchKernelGGL(relayout_kernel, dim3(b.blocks), dim3(kThreads), 0, stream, b);
 }
 
-void launch_norm_rope(const NormRopeArgs &a, int lanes, int dtype, uint32_t blocks, hipStream_t stream) {
-#define ULY_NR(L, T)                                                                             \
-    if (lanes == L && dtype == T) {                                                              \
-        hipLaunchKernelGGL((norm_rope_kernel<L, T>), dim3(blocks), dim3(kThreads), 0, stream, a); \
-        return;                                                                                  \
+template <int L, int T>
+static void launch_norm_rope_lanes(const NormRopeArgs &a, bool uniform, bool tile, uint32_t blocks,
+                                   hipStream_t stream) {
+    const dim3 grid(blocks), block(kRopeThreads);
+    if (uniform && tile) hipLaunchKernelGGL((norm_rope_kernel<L, T, true, true>), grid, block, 0, stream, a);
+    else if (uniform) hipLaunchKernelGGL((norm_rope_kernel<L, T, true, false>), grid, block, 0, stream, a);
+    else if (tile) hipLaunchKernelGGL((norm_rope_kernel<L, T, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((norm_rope_kernel<L, T, false, false>), grid, block, 0, stream, a);
+}
+
+void launch_norm_rope(const NormRopeArgs &a, int lanes, int dtype, bool uniform, bool tile, uint32_t blocks,
+                      hipStream_t stream) {
+    const bool bf = dtype == 2;
+    switch (lanes) {
+    case 4: bf ? launch_norm_rope_lanes<4, 2>(a, uniform, tile, blocks, stream)
+               : launch_norm_rope_lanes<4, 1>(a, uniform, tile, blocks, stream); break;
+    case 8: bf ? launch_norm_rope_lanes<8, 2>(a, uniform, tile, blocks, stream)
+               : launch_norm_rope_lanes<8, 1>(a, uniform, tile, blocks, stream); break;
+    case 16: bf ? launch_norm_rope_lanes<16, 2>(a, uniform, tile, blocks, stream)
+                : launch_norm_rope_lanes<16, 1>(a, uniform, tile, blocks, stream); break;
+    default: bf ? launch_norm_rope_lanes<32, 2>(a, uniform, tile, blocks, stream)
+                : launch_norm_rope_lanes<32, 1>(a, uniform, tile, blocks, stream); break;
     }
-    ULY_NR(4, 1) ULY_NR(8, 1) ULY_NR(16, 1) ULY_NR(32, 1)
-    ULY_NR(4, 2) ULY_NR(8, 2) ULY_NR(16, 2) ULY_NR(32, 2)
-#undef ULY_NR
 }
 
 void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream) {

@@ -56,8 +56,7 @@ struct Target {
 };
 
 struct Pending {
-    hipStream_t stream;
-    hipEvent_t ev;
+    hipStream_t stream;   // a stream that carries work of the current group
 };
 
 struct ProfRecord {
@@ -160,7 +159,7 @@ struct uly_ctx {
     std::vector<Target> targets;
     std::vector<Pending> pending;
     std::vector<hipEvent_t> sync_pool;
-    bool profiling = false;
+    int profile_mask = 0;   // bit k: bracket kernels of kind k with timing events
     std::vector<ProfRecord> prof;
     std::vector<hipEvent_t> timing_pool;
     uly_stats stats{};
@@ -256,7 +255,8 @@ uly_status launch(uly_ctx *c, int kind, hipStream_t s, F &&enqueue) {
     (void)hipGetLastError();   // clear a stale error left by someone else's call
     hipEvent_t e0 = nullptr, e1 = nullptr;
     hipError_t err = hipSuccess;
-    if (c->profiling) {
+    const bool timed = (c->profile_mask >> kind) & 1;
+    if (timed) {
         e0 = take_event(c->timing_pool, hipEventDefault, err);
         if (!e0) return poison(c, err, "hipEventCreate");
         e1 = take_event(c->timing_pool, hipEventDefault, err);
@@ -266,7 +266,7 @@ uly_status launch(uly_ctx *c, int kind, hipStream_t s, F &&enqueue) {
     enqueue();
     err = hipGetLastError();
     if (err != hipSuccess) return poison(c, err, "kernel launch");
-    if (c->profiling) {
+    if (timed) {
         if ((err = hipEventRecord(e1, s)) != hipSuccess) return poison(c, err, "hipEventRecord");
         c->prof.push_back({kind, e0, e1, -1.0});
     }
@@ -274,19 +274,15 @@ uly_status launch(uly_ctx *c, int kind, hipStream_t s, F &&enqueue) {
     return ULY_OK;
 }
 
-// Record that `s` carries work of the current group (one event per stream).
+// Note that `s` carries work of the current group.  The event that the
+// consumer waits on is recorded at uly_wait time, and only for streams other
+// than the consumer's, so a group that runs entirely on the consumer's
+// stream costs no event at all.
 uly_status mark_pending(uly_ctx *c, hipStream_t s) {
-    hipError_t err = hipSuccess;
     for (auto &p : c->pending)
-        if (p.stream == s) {
-            err = hipEventRecord(p.ev, s);
-            return err == hipSuccess ? ULY_OK : poison(c, err, "hipEventRecord");
-        }
-    hipEvent_t e = take_event(c->sync_pool, hipEventDisableTiming, err);
-    if (!e) return poison(c, err, "hipEventCreate");
-    c->pending.push_back({s, e});
-    err = hipEventRecord(e, s);
-    return err == hipSuccess ? ULY_OK : poison(c, err, "hipEventRecord");
+        if (p.stream == s) return ULY_OK;
+    c->pending.push_back({s});
+    return ULY_OK;
 }
 
 // The comm stream waits for everything enqueued on `caller` so far (input
@@ -437,7 +433,6 @@ uly_status uly_destroy(uly_ctx *c) {
         DeviceGuard g(c->device);
         if (c->comm && hipStreamSynchronize(c->comm) != hipSuccess)
             st = fail(ULY_E_HIP, "hipStreamSynchronize on destroy failed");
-        for (auto &p : c->pending) (void)hipEventDestroy(p.ev);
         for (auto e : c->sync_pool) (void)hipEventDestroy(e);
         for (auto &r : c->prof) {
             (void)hipEventDestroy(r.start);
@@ -559,22 +554,23 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
     return mark_pending(c, c->comm);
 }
 
-uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly_tensor *k, const void *w_q,
-                                      const void *w_k, float eps, const float *cos_tab,
-                                      const float *sin_tab, int64_t table_rows, const char *const tags[2],
-                                      void *const outs[2], hipStream_t caller) {
+uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly_tensor *k, const uly_tensor *v,
+                                      const void *w_q, const void *w_k, float eps, const float *cos_tab,
+                                      const float *sin_tab, int64_t table_rows, const char *const tags[3],
+                                      void *const outs[3], hipStream_t caller) {
     uly_status st = ctx_ok(c);
     if (st != ULY_OK) return st;
-    const uly_tensor *mem[2] = {q, k};
-    const void *wts[2] = {w_q, w_k};
-    const char *names[2] = {"q", "k"};
-    Operand ops[2];
-    uint8_t *dsts[2] = {nullptr, nullptr};
+    const uly_tensor *mem[3] = {q, k, v};
+    const void *wts[3] = {w_q, w_k, nullptr};
+    const char *names[3] = {"q", "k", "v"};
+    Operand ops[3];
+    uint8_t *dsts[3] = {nullptr, nullptr, nullptr};
     int present = 0, dtype = 0;
     int64_t B = -1, S = -1, D = -1;
     std::vector<Range> in_ranges, out_ranges;
     if (!(eps > 0.f) || !std::isfinite(eps)) return fail(ULY_E_INVAL, "eps must be a positive finite value");
-    for (int i = 0; i < 2; ++i) {
+    // Every member is checked and resolved before anything is enqueued.
+    for (int i = 0; i < 3; ++i) {
         if (!mem[i]) continue;
         if ((st = check_operand(mem[i], names[i], c->P, ops[i])) != ULY_OK) return st;
         const Operand &x = ops[i];
@@ -584,12 +580,12 @@ uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly
         if (present == 0) {
             dtype = x.dtype; B = x.B; S = x.S; D = x.D;
         } else {
-            if (x.dtype != dtype) return fail(ULY_E_DTYPE, "%s: dtype differs from q", names[i]);
+            if (x.dtype != dtype) return fail(ULY_E_DTYPE, "%s: dtype differs from the other members", names[i]);
             if (x.B != B || x.S != S || x.D != D)
-                return fail(ULY_E_INVAL, "%s: B, S_l and D must match q", names[i]);
+                return fail(ULY_E_INVAL, "%s: B, S_l and D must match the other members", names[i]);
         }
         ++present;
-        if (!wts[i] || !aligned16(wts[i]))
+        if (i < 2 && (!wts[i] || !aligned16(wts[i])))
             return fail(ULY_E_INVAL, "%s: weight pointer null or not 16-byte aligned", names[i]);
     }
     if (present == 0) return fail(ULY_E_INVAL, "no operand given");
@@ -601,7 +597,7 @@ uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly
     if (table_rows < int64_t(c->P) * S)
         return fail(ULY_E_INVAL, "table has %lld rows, positions reach %lld", (long long)table_rows,
                     (long long)(int64_t(c->P) * S));
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 3; ++i) {
         if (!mem[i] || ops[i].empty()) continue;
         const Operand &x = ops[i];
         const int64_t tshape[4] = {x.B, x.S * c->P, x.H / c->P, x.D};
@@ -611,15 +607,15 @@ uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly
         in_ranges.push_back(x.range);
         out_ranges.push_back(dense_range(dsts[i], int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3]));
     }
-    in_ranges.push_back(dense_range(cos_tab, table_rows * D));   // fp32 [rows][D/2] = 2*rows*D/2 halves
+    in_ranges.push_back(dense_range(cos_tab, table_rows * D));   // fp32 [rows][D/2] = rows*D halves
     in_ranges.push_back(dense_range(sin_tab, table_rows * D));
-    in_ranges.push_back(dense_range(w_q ? w_q : cos_tab, w_q ? D : 0));
-    in_ranges.push_back(dense_range(w_k ? w_k : cos_tab, w_k ? D : 0));
+    if (w_q) in_ranges.push_back(dense_range(w_q, D));
+    if (w_k) in_ranges.push_back(dense_range(w_k, D));
     if ((st = check_overlaps(in_ranges, out_ranges)) != ULY_OK) return st;
 
     NormRopeArgs a{};
-    uint32_t Hsum = 0;
-    for (int i = 0; i < 2; ++i) {
+    uint32_t Hrows[3] = {0, 0, 0};
+    for (int i = 0; i < 3; ++i) {
         NormRopeOperand &o = a.op[i];
         o = NormRopeOperand{};
         o.hl = FastDiv::make(1);
@@ -638,32 +634,37 @@ uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly
         o.d_g = Hl * x.D;
         o.hl = FastDiv::make(uint32_t(Hl));
         o.H = uint32_t(x.H);
-        Hsum += uint32_t(x.H);
+        Hrows[i] = uint32_t(x.H);
     }
-    const bool has_q = mem[0] && !ops[0].empty();
-    const int64_t rows = int64_t(c->P) * B * S * Hsum;
+    const uint32_t Hsum = Hrows[0] + Hrows[1] + Hrows[2];
+    const int64_t tokens = int64_t(c->P) * B * S;
     if (c->host_only) return host_only_launch(c);
-    if (rows == 0) return ULY_OK;
-    if (rows >= kMaxVecs || int64_t(c->P) * S >= kMaxVecs)
-        return fail(ULY_E_UNSUPPORTED, "too many rows for one launch (%lld)", (long long)rows);
+    if (tokens == 0) return ULY_OK;
+    if (tokens * Hsum >= kMaxVecs || tokens >= kMaxVecs)
+        return fail(ULY_E_UNSUPPORTED, "too many rows for one launch (%lld)", (long long)(tokens * Hsum));
     a.cos_tab = cos_tab;
     a.sin_tab = sin_tab;
     a.rpt = FastDiv::make(Hsum);
     a.sl = FastDiv::make(uint32_t(S));
     a.bdiv = FastDiv::make(uint32_t(B));
-    a.H0 = has_q ? a.op[0].H : 0u;
-    a.rows = uint32_t(rows);
+    a.H0 = Hrows[0];
+    a.H01 = Hrows[0] + Hrows[1];
+    a.tokens = uint32_t(tokens);
     a.S_l = uint32_t(S);
     a.D = uint32_t(D);
-    const uint32_t groups = uint32_t(kThreads / lanes);
-    a.rows_per_block = groups * kRopeUnroll * kRopeItersPerBlock;
     a.eps = eps;
     a.inv_D = 1.0f / float(D);
-    const uint32_t blocks = uint32_t((rows + a.rows_per_block - 1) / a.rows_per_block);
+    const uint32_t blocks = uint32_t((tokens + kRopeTokens - 1) / kRopeTokens);
+    // A wave holds 64 / lanes consecutive row slots; when every operand's
+    // head count is a multiple of that, no wave straddles two operands.
+    const uint32_t per_wave = uint32_t(64 / lanes);
+    const bool uniform = Hrows[0] % per_wave == 0 && Hrows[1] % per_wave == 0 && Hrows[2] % per_wave == 0;
+    // Tiles that never cross a rank or batch boundary need one decode per block.
+    const bool tile = S % kRopeTokens == 0;
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
     if ((st = launch(c, ULY_K_NORM_ROPE, caller,
-                     [&] { launch_norm_rope(a, lanes, dtype, blocks, caller); })) != ULY_OK)
+                     [&] { launch_norm_rope(a, lanes, dtype, uniform, tile, blocks, caller); })) != ULY_OK)
         return st;
     return mark_pending(c, caller);
 }
@@ -678,11 +679,13 @@ uly_status uly_wait(uly_ctx *c, hipStream_t consumer) {
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
     for (auto &p : c->pending) {
-        if (p.stream != consumer) {
-            hipError_t err = hipStreamWaitEvent(consumer, p.ev, 0);
-            if (err != hipSuccess) return poison(c, err, "hipStreamWaitEvent");
-        }
-        c->sync_pool.push_back(p.ev);
+        if (p.stream == consumer) continue;       // stream order already covers it
+        hipError_t err = hipSuccess;
+        hipEvent_t e = take_event(c->sync_pool, hipEventDisableTiming, err);
+        if (!e) return poison(c, err, "hipEventCreate");
+        c->sync_pool.push_back(e);                // reusable once the wait below is enqueued
+        if ((err = hipEventRecord(e, p.stream)) != hipSuccess) return poison(c, err, "hipEventRecord");
+        if ((err = hipStreamWaitEvent(consumer, e, 0)) != hipSuccess) return poison(c, err, "hipStreamWaitEvent");
     }
     c->pending.clear();
     return ULY_OK;
@@ -892,10 +895,10 @@ uly_status uly_rope_table_3d(float *cos_out, float *sin_out, int64_t rows, int64
 
 // ---- measurement and test hooks ------------------------------------------------
 
-uly_status uly_profile_enable(uly_ctx *c, int on) {
+uly_status uly_profile_enable(uly_ctx *c, int kind_mask) {
     uly_status st = ctx_ok(c);
     if (st != ULY_OK) return st;
-    c->profiling = on != 0;
+    c->profile_mask = kind_mask & ((1 << ULY_K_COUNT) - 1);
     return ULY_OK;
 }
 

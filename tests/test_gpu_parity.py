@@ -187,21 +187,29 @@ FUSED_SMALL = [
 def test_fused_norm_rope_small(dev, orc, P, B, S_l, Hq, Hkv, D, dtype, fused):
     if fused:
         qkv = synth.normal((P, B, S_l, 3, Hq, D), dtype, 21, dev)
-        q, k = qkv[:, :, :, 0], qkv[:, :, :, 1]
+        q, k, v = qkv[:, :, :, 0], qkv[:, :, :, 1], qkv[:, :, :, 2]
     else:
-        q, k, _ = contiguous_qkv(P, B, S_l, Hq, D, dtype, 21, dev, Hkv)
+        q, k, v = contiguous_qkv(P, B, S_l, Hq, D, dtype, 21, dev, Hkv)
     w_q = synth.norm_weight(D, dtype, 1, dev)
     w_k = synth.norm_weight(D, dtype, 2, dev)
     rows = P * S_l + 5
     cos, sin = rope_table_1d(rows, D)
     ocos, osin = orc.rope_table_1d(rows, D)
     with UlyssesContext(P, device=0) as ctx:
-        yq, yk = ctx.fused_qk_norm_rope_scatter(q, k, w_q, w_k, cos.to(dev), sin.to(dev))
+        yq, yk, yv = ctx.fused_qk_norm_rope_scatter(q, k, w_q, w_k, cos.to(dev), sin.to(dev), v=v)
         ctx.wait()
         torch.cuda.synchronize()
         for x, w, y, name in ((q, w_q, yq, "q"), (k, w_k, yk, "k")):
             ref = orc.fused_norm_rope_scatter(to_bits(x), dtype, to_bits(w), 1e-6, ocos, osin)
             assert_close16(y, ref, dtype, name)
+        # V rides in the same launch and is moved bit for bit
+        np.testing.assert_array_equal(to_bits(yv), orc.scatter(to_bits(v)))
+        # Q/K without V give the same bits as with it
+        yq2, yk2, _ = ctx.fused_qk_norm_rope_scatter(q, k, w_q, w_k, cos.to(dev), sin.to(dev),
+                                                     tags=("q2", "k2", None))
+        torch.cuda.synchronize()
+        assert torch.equal(yq2.view(torch.int16), yq.view(torch.int16))
+        assert torch.equal(yk2.view(torch.int16), yk.view(torch.int16))
 
 
 def test_fused_single_operand_and_determinism(dev, orc):
@@ -211,8 +219,8 @@ def test_fused_single_operand_and_determinism(dev, orc):
     cos, sin = rope_table_1d(P * S_l, D)
     cos, sin = cos.to(dev), sin.to(dev)
     with UlyssesContext(P, device=0) as ctx:
-        _, y1 = ctx.fused_qk_norm_rope_scatter(None, k, None, w, cos, sin, tags=(None, "k1"))
-        _, y2 = ctx.fused_qk_norm_rope_scatter(None, k, None, w, cos, sin, tags=(None, "k2"))
+        _, y1, _ = ctx.fused_qk_norm_rope_scatter(None, k, None, w, cos, sin, tags=(None, "k1"))
+        _, y2, _ = ctx.fused_qk_norm_rope_scatter(None, k, None, w, cos, sin, tags=(None, "k2"))
         ctx.wait()
         torch.cuda.synchronize()
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
@@ -231,7 +239,7 @@ def test_fused_edge_rows(dev, orc):
     w = synth.norm_weight(D, "bf16", 4, dev)
     cos, sin = rope_table_1d(P * S_l, D)
     with UlyssesContext(P, device=0) as ctx:
-        (y, _) = ctx.fused_qk_norm_rope_scatter(xd, None, w, None, cos.to(dev), sin.to(dev))
+        (y, _, _) = ctx.fused_qk_norm_rope_scatter(xd, None, w, None, cos.to(dev), sin.to(dev))
         ctx.wait()
         torch.cuda.synchronize()
     ocos, osin = orc.rope_table_1d(P * S_l, D)
@@ -287,7 +295,7 @@ def test_video_dit_block_full(dev, orc):
     o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 3, dev)
     with UlyssesContext(P, device=0) as ctx:
         _, _, yv = ctx.scatter_qkv(v=qkv[:, :, :, 2])
-        yq, yk = ctx.fused_qk_norm_rope_scatter(qkv[:, :, :, 0], qkv[:, :, :, 1], w_q, w_k,
+        yq, yk, _ = ctx.fused_qk_norm_rope_scatter(qkv[:, :, :, 0], qkv[:, :, :, 1], w_q, w_k,
                                                 cos.to(dev), sin.to(dev), eps=w.eps)
         ctx.wait()
         z = ctx.gather_out(o)
@@ -300,6 +308,26 @@ def test_video_dit_block_full(dev, orc):
             ref = orc.fused_norm_rope_scatter(xb[:, :, :, c], "bf16", to_bits(wt), w.eps, ocos, osin)
             e = assert_close16(y, ref, "bf16", name)
             print("video-DiT %s max-abs error %.3g" % (name, e))
+
+
+def test_video_dit_block_single_launch_full(dev, orc):
+    """The same block with V scattered inside the fused Q/K launch."""
+    w = synth.VIDEO_DIT
+    P, B, S_l, H, D = w.P, w.B, w.S_l, w.Hq, w.D
+    qkv = synth.normal((P, B, S_l, 3, H, D), "bf16", 5, dev)
+    w_q, w_k = synth.norm_weight(D, "bf16", 6, dev), synth.norm_weight(D, "bf16", 7, dev)
+    cos, sin = rope_table_1d(P * S_l, D, theta=w.theta)
+    with UlyssesContext(P, device=0) as ctx:
+        yq, yk, yv = ctx.fused_qk_norm_rope_scatter(qkv[:, :, :, 0], qkv[:, :, :, 1], w_q, w_k, cos.to(dev),
+                                                    sin.to(dev), eps=w.eps, v=qkv[:, :, :, 2])
+        ctx.wait()
+        torch.cuda.synchronize()
+        xb = to_bits(qkv)
+        np.testing.assert_array_equal(to_bits(yv), orc.scatter(xb[:, :, :, 2]))
+        ocos, osin = orc.rope_table_1d(P * S_l, D, theta=w.theta)
+        for c, wt, y, name in ((0, w_q, yq, "q"), (1, w_k, yk, "k")):
+            ref = orc.fused_norm_rope_scatter(xb[:, :, :, c], "bf16", to_bits(wt), w.eps, ocos, osin)
+            assert_close16(y, ref, "bf16", name)
 
 
 def test_wan_long_sequence_full(dev, orc):
@@ -320,7 +348,7 @@ def test_wan_long_sequence_full(dev, orc):
         fb_v = to_bits(fulls[2])
         np.testing.assert_array_equal(xb_v, orc.pad_shard(fb_v, P, S_l))
         _, _, yv = ctx.scatter_qkv(v=shards[2])
-        yq, yk = ctx.fused_qk_norm_rope_scatter(shards[0], shards[1], w_q, w_k, cos.to(dev), sin.to(dev))
+        yq, yk, _ = ctx.fused_qk_norm_rope_scatter(shards[0], shards[1], w_q, w_k, cos.to(dev), sin.to(dev))
         ctx.wait()
         torch.cuda.synchronize()
         win = _windows(S_l, 4, 64, 1) + [(S_l - 176 - 8, S_l)]      # include the padded tail
@@ -430,7 +458,7 @@ def test_consumer_on_other_stream_sees_results(dev, orc):
     consumer = torch.cuda.Stream()
     with UlyssesContext(P, device=0) as ctx:
         _, _, yv = ctx.scatter_qkv(v=v)
-        yq, yk = ctx.fused_qk_norm_rope_scatter(q, k, w_q, w_k, cos.to(dev), sin.to(dev))
+        yq, yk, _ = ctx.fused_qk_norm_rope_scatter(q, k, w_q, w_k, cos.to(dev), sin.to(dev))
         ctx.wait(consumer)
         with torch.cuda.stream(consumer):
             snap = [yq.clone(), yk.clone(), yv.clone()]

@@ -219,10 +219,11 @@ def test_missing_and_mistyped_targets(lib, ctx4):
 
 
 def _fused(lib, c, q, k, w=(BASE + 200 * MiB, BASE + 201 * MiB), eps=1e-6, rows=64,
-           tabs=(BASE + 300 * MiB, BASE + 310 * MiB), outs=(BASE + 100 * MiB, BASE + 120 * MiB)):
-    args = [ctypes.byref(x) if x is not None else None for x in (q, k)]
+           tabs=(BASE + 300 * MiB, BASE + 310 * MiB), outs=(BASE + 100 * MiB, BASE + 120 * MiB, BASE + 140 * MiB),
+           v=None):
+    args = [ctypes.byref(x) if x is not None else None for x in (q, k, v)]
     return lib.fused_qk_norm_rope_scatter(c.h, *args, w[0], w[1], eps, tabs[0], tabs[1], rows,
-                                          _lib.tags_array(("q", "k")), _lib.ptr_array(outs), None)
+                                          _lib.tags_array(("q", "k", "v")), _lib.ptr_array(outs), None)
 
 
 def test_fused_rejections(lib, ctx4):
@@ -241,6 +242,14 @@ def test_fused_rejections(lib, ctx4):
     # GQA: Q and K may differ in heads
     k2 = T(BASE + 64 * MiB, (1, 16, 4, 128))
     assert _fused(lib, ctx4, q, k2) == _lib.E_UNSUPPORTED and b"host-only" in lib.uly_last_error()
+    # V rides along unchanged; it needs no weight but must match B, S_l, D, dtype
+    v = T(BASE + 80 * MiB, (1, 16, 4, 128))
+    assert _fused(lib, ctx4, q, k2, v=v) == _lib.E_UNSUPPORTED
+    assert _fused(lib, ctx4, None, None, v=v) == _lib.E_UNSUPPORTED
+    v_bad = T(BASE + 80 * MiB, (1, 16, 4, 128), dtype=_lib.F16)
+    assert _fused(lib, ctx4, q, k2, v=v_bad) == _lib.E_DTYPE
+    v_over = T(BASE + 100 * MiB, (1, 16, 4, 128))         # reads what q's target is written to
+    assert _fused(lib, ctx4, q, k2, v=v_over) == _lib.E_OVERLAP
 
 
 def test_fail_stop_after_launch_failure(lib):
