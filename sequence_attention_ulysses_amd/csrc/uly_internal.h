@@ -12,18 +12,19 @@ namespace uly {
 
 // ---------------------------------------------------------------------------
 // Chunk relayout.  A Ulysses exchange moves contiguous chunks of Hl*D
-// elements (one token's head band) between two 4-D index spaces.  The
-// destination is always dense in the plan's iteration order, so a thread's
-// flat 16-byte vector index i gives its destination directly (dst + 16*i)
-// and its source through the 4 outer indices (i0 outermost) and the vector
-// position c inside the chunk:
+// elements (one token's head band) between two 4-D index spaces.  A
+// thread's flat 16-byte vector index i splits into 4 outer indices (i0
+// outermost) and the vector position c inside the chunk,
 //   i = (((i0*n1 + i1)*n2 + i2)*n3 + i3)*vpc + c
-//   src = base + i0*ss[0] + i1*ss[1] + i2*ss[2] + i3*ss[3] + 16*c   (bytes)
+//   src = src_base + i0*ss[0] + i1*ss[1] + i2*ss[2] + i3*ss[3] + 16*c   (bytes)
+//   dst = dst_base + i0*ds[0] + i1*ds[1] + i2*ds[2] + i3*ds[3] + 16*c
+// The planner picks which side is dense in i.
 // ---------------------------------------------------------------------------
 struct CopyPlan {
     const uint8_t *src;
     uint8_t *dst;
     int64_t ss[4];
+    int64_t ds[4];
     FastDiv vpc;         // 16-byte vectors per chunk
     FastDiv n3, n2, n1;  // extents of the inner three outer dims
     uint32_t total;      // vectors in this plan
@@ -116,7 +117,7 @@ void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
 #define ULY_COPY_UNROLL 4
 #endif
 #ifndef ULY_ROPE_TOKENS
-#define ULY_ROPE_TOKENS 4
+#define ULY_ROPE_TOKENS 2
 #endif
 #ifndef ULY_ROPE_THREADS
 #define ULY_ROPE_THREADS 512

@@ -81,6 +81,7 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(CopyBatch b) {
 
     const uint32_t first = (bid - P.first_block) * kCopyVecsPerBlock + threadIdx.x;
     uint4 v[kCopyUnroll];
+    uint8_t *d[kCopyUnroll];
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
         const uint32_t i = first + u * kThreads;
@@ -92,13 +93,15 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(CopyBatch b) {
             P.n1.divmod(t, i0, i1);
             const uint8_t *s = P.src + int64_t(i0) * P.ss[0] + int64_t(i1) * P.ss[1] +
                                int64_t(i2) * P.ss[2] + int64_t(i3) * P.ss[3] + uint64_t(c) * 16u;
+            d[u] = P.dst + int64_t(i0) * P.ds[0] + int64_t(i1) * P.ds[1] + int64_t(i2) * P.ds[2] +
+                   int64_t(i3) * P.ds[3] + uint64_t(c) * 16u;
             v[u] = load16(s);
         }
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
         const uint32_t i = first + u * kThreads;
-        if (i < P.total) store16(P.dst + uint64_t(i) * 16u, v[u]);
+        if (i < P.total) store16(d[u], v[u]);
     }
 }
 
@@ -178,8 +181,14 @@ __device__ __forceinline__ T sel3(uint32_t i, T a, T b, T c) {
 // Rows of operand 2 (V) ride in the same grid as plain 16-byte copies: the
 // whole Q/K/V scatter is one launch that shares HBM bandwidth without a
 // second kernel's ramp-up and tail.
+#ifdef ULY_ROPE_WAVES_PER_EU
+#define ULY_ROPE_OCCUPANCY __attribute__((amdgpu_waves_per_eu(ULY_ROPE_WAVES_PER_EU)))
+#else
+#define ULY_ROPE_OCCUPANCY
+#endif
+
 template <int LANES, int DT, bool UNI, bool TILE>
-__global__ __launch_bounds__(kRopeThreads) void norm_rope_kernel(NormRopeArgs a) {
+__global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_kernel(NormRopeArgs a) {
     constexpr int GROUPS = kRopeThreads / LANES;
     constexpr int TU = kRopeTokens;
     const uint32_t lane = threadIdx.x % LANES;

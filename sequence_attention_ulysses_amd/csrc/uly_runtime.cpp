@@ -294,51 +294,74 @@ uly_status fork_comm(uly_ctx *c, hipStream_t caller) {
     return err == hipSuccess ? ULY_OK : poison(c, err, "hipStreamWaitEvent");
 }
 
-// Plan of one scatter member: rank-major source [P][B][S_l][H][D] (strided)
-// -> dense [P(q)][B][P(r)*S_l][Hl][D]; iteration (q, b, r, s, chunk vector).
+#ifndef ULY_SCATTER_ORDER
+#define ULY_SCATTER_ORDER 0
+#endif
+#ifndef ULY_GATHER_ORDER
+#define ULY_GATHER_ORDER 0
+#endif
+
+// Fill a plan from 4 (extent, source stride, destination stride) dims,
+// outermost first; strides in bytes.
+void fill_plan(CopyPlan &p, const uint8_t *src, uint8_t *dst, const int64_t n[4], const int64_t ss[4],
+               const int64_t ds[4], int64_t vpc, int64_t total) {
+    p = CopyPlan{};
+    p.src = src;
+    p.dst = dst;
+    for (int k = 0; k < 4; ++k) {
+        p.ss[k] = ss[k];
+        p.ds[k] = ds[k];
+    }
+    p.vpc = FastDiv::make(uint32_t(vpc));
+    p.n1 = FastDiv::make(uint32_t(n[1]));
+    p.n2 = FastDiv::make(uint32_t(n[2]));
+    p.n3 = FastDiv::make(uint32_t(n[3]));
+    p.total = uint32_t(total);
+}
+
+// Plan of one scatter member: rank-major source [P(r)][B][S_l][H][D]
+// (strided) -> dense [P(q)][B][P(r)*S_l][Hl][D].  A chunk is one token's
+// head band q: Hl*D elements.
 uly_status plan_scatter(const Operand &x, int P, uint8_t *dst, CopyPlan &p) {
-    const int64_t Hl = x.H / P;
-    const int64_t chunk_bytes = Hl * x.D * 2;
-    const int64_t vpc = chunk_bytes / 16;
-    const int64_t total = int64_t(P) * x.B * P * x.S * vpc;
+    const int64_t Hl = x.H / P, S = int64_t(P) * x.S;
+    const int64_t C = Hl * x.D * 2;    // chunk bytes
+    const int64_t total = int64_t(P) * x.B * P * x.S * (C / 16);
     if (total >= kMaxVecs || x.S >= kMaxVecs || x.B >= kMaxVecs)
         return fail(ULY_E_UNSUPPORTED, "operand too large for one launch (%lld vectors)", (long long)total);
-    p = CopyPlan{};
-    p.src = x.data;
-    p.dst = dst;
-    p.ss[0] = Hl * x.sh * 2;          // q: head band offset
-    p.ss[1] = x.sb * 2;               // b
-    p.ss[2] = x.rank_stride * 2;      // r: source rank slab
-    p.ss[3] = x.ss * 2;               // s
-    p.vpc = FastDiv::make(uint32_t(vpc));
-    p.n1 = FastDiv::make(uint32_t(x.B));
-    p.n2 = FastDiv::make(uint32_t(P));
-    p.n3 = FastDiv::make(uint32_t(x.S));
-    p.total = uint32_t(total);
+    // per-dim (source, destination) byte strides
+    const int64_t q_s = Hl * x.sh * 2, q_d = x.B * S * C;
+    const int64_t b_s = x.sb * 2, b_d = S * C;
+    const int64_t r_s = x.rank_stride * 2, r_d = x.S * C;
+    const int64_t s_s = x.ss * 2, s_d = C;
+    if (ULY_SCATTER_ORDER == 0) {     // destination order (q, b, r, s)
+        const int64_t n[4] = {P, x.B, P, x.S}, ss[4] = {q_s, b_s, r_s, s_s}, ds[4] = {q_d, b_d, r_d, s_d};
+        fill_plan(p, x.data, dst, n, ss, ds, C / 16, total);
+    } else {                          // source order (r, b, s, q)
+        const int64_t n[4] = {P, x.B, x.S, P}, ss[4] = {r_s, b_s, s_s, q_s}, ds[4] = {r_d, b_d, s_d, q_d};
+        fill_plan(p, x.data, dst, n, ss, ds, C / 16, total);
+    }
     return ULY_OK;
 }
 
 // Plan of the inverse: head-sharded [P(q)][B][S][Hl][D] (strided) -> dense
-// [P(r)][B][S_l][P(q)*Hl][D]; iteration (r, b, s, q, chunk vector).
+// [P(r)][B][S_l][P(q)*Hl][D].
 uly_status plan_gather(const Operand &o, int P, uint8_t *dst, CopyPlan &p) {
-    const int64_t S_l = o.S / P;
-    const int64_t chunk_bytes = o.H * o.D * 2;
-    const int64_t vpc = chunk_bytes / 16;
-    const int64_t total = int64_t(P) * o.B * S_l * P * vpc;
+    const int64_t S_l = o.S / P, H = o.H * P;
+    const int64_t C = o.H * o.D * 2;
+    const int64_t total = int64_t(P) * o.B * S_l * P * (C / 16);
     if (total >= kMaxVecs || o.S >= kMaxVecs || o.B >= kMaxVecs)
         return fail(ULY_E_UNSUPPORTED, "operand too large for one launch (%lld vectors)", (long long)total);
-    p = CopyPlan{};
-    p.src = o.data;
-    p.dst = dst;
-    p.ss[0] = S_l * o.ss * 2;         // r: destination rank's sequence block
-    p.ss[1] = o.sb * 2;               // b
-    p.ss[2] = o.ss * 2;               // s
-    p.ss[3] = o.rank_stride * 2;      // q: source rank slab (head band)
-    p.vpc = FastDiv::make(uint32_t(vpc));
-    p.n1 = FastDiv::make(uint32_t(o.B));
-    p.n2 = FastDiv::make(uint32_t(S_l));
-    p.n3 = FastDiv::make(uint32_t(P));
-    p.total = uint32_t(total);
+    const int64_t r_s = S_l * o.ss * 2, r_d = o.B * S_l * H * o.D * 2;
+    const int64_t b_s = o.sb * 2, b_d = S_l * H * o.D * 2;
+    const int64_t s_s = o.ss * 2, s_d = H * o.D * 2;
+    const int64_t q_s = o.rank_stride * 2, q_d = C;
+    if (ULY_GATHER_ORDER == 0) {      // destination order (r, b, s, q)
+        const int64_t n[4] = {P, o.B, S_l, P}, ss[4] = {r_s, b_s, s_s, q_s}, ds[4] = {r_d, b_d, s_d, q_d};
+        fill_plan(p, o.data, dst, n, ss, ds, C / 16, total);
+    } else {                          // source order (q, b, r, s)
+        const int64_t n[4] = {P, o.B, P, S_l}, ss[4] = {q_s, b_s, r_s, s_s}, ds[4] = {q_d, b_d, r_d, s_d};
+        fill_plan(p, o.data, dst, n, ss, ds, C / 16, total);
+    }
     return ULY_OK;
 }
 
