@@ -180,6 +180,8 @@ FUSED_SMALL = [
     (2, 1, 50, 4, 4, 256, "f16", False),
     (4, 1, 29, 8, 8, 32, "bf16", True),
     (1, 1, 64, 4, 4, 128, "bf16", False),
+    (2, 1, 40, 6, 2, 128, "bf16", False),     # head counts not a multiple of the groups per wave
+    (3, 1, 16, 6, 3, 128, "f16", False),
 ]
 
 
@@ -515,3 +517,99 @@ def test_device_fail_stop(dev):
     with pytest.raises(UlyBroken):
         ctx.scatter_qkv(q=q)
     ctx.close()
+
+
+def test_two_stream_and_single_launch_agree(dev):
+    """V on the comm stream and V inside the fused launch give the same bits, and so
+    do the Q/K targets of both forms."""
+    P, B, S_l, H, D = 4, 1, 256, 8, 128
+    qkv = synth.normal((P, B, S_l, 3, H, D), "bf16", 90, dev)
+    w_q, w_k = synth.norm_weight(D, "bf16", 91, dev), synth.norm_weight(D, "bf16", 92, dev)
+    cos, sin = (t.to(dev) for t in rope_table_1d(P * S_l, D))
+    with UlyssesContext(P, device=0) as ctx:
+        a = ctx.fused_qk_norm_rope_scatter(qkv[:, :, :, 0], qkv[:, :, :, 1], w_q, w_k, cos, sin, v=qkv[:, :, :, 2],
+                                           tags=("qa", "ka", "va"))
+        (_, _, vb) = ctx.scatter_qkv(v=qkv[:, :, :, 2], tags=(None, None, "vb"))
+        qb, kb, _ = ctx.fused_qk_norm_rope_scatter(qkv[:, :, :, 0], qkv[:, :, :, 1], w_q, w_k, cos, sin,
+                                                   tags=("qb", "kb", None))
+        ctx.wait()
+        torch.cuda.synchronize()
+        for x, y in zip(a, (qb, kb, vb)):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_two_contexts_in_flight(dev, orc):
+    """Two groups on two streams, submissions interleaved, each consumed on its own stream."""
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    x1 = synth.normal((2, 1, 300, 8, 64), "f16", 93, dev)
+    x2 = synth.normal((4, 2, 100, 8, 128), "bf16", 94, dev)
+    torch.cuda.synchronize()
+    c1, c2 = UlyssesContext(2, device=0), UlyssesContext(4, device=0)
+    try:
+        for _ in range(3):
+            y1 = c1.scatter_qkv(q=x1, k=x1, stream=s1)
+            y2 = c2.scatter_qkv(v=x2, stream=s2)
+            c1.wait(s1)
+            c2.wait(s2)
+            with torch.cuda.stream(s1):
+                z1 = c1.gather_out(y1[0], stream=s1)
+            with torch.cuda.stream(s2):
+                z2 = c2.gather_out(y2[2], stream=s2)
+        s1.synchronize()
+        s2.synchronize()
+        np.testing.assert_array_equal(to_bits(y1[1]), orc.scatter(to_bits(x1)))
+        np.testing.assert_array_equal(to_bits(y2[2]), orc.scatter(to_bits(x2)))
+        assert torch.equal(z1.view(torch.int16), x1.view(torch.int16))
+        assert torch.equal(z2.view(torch.int16), x2.view(torch.int16))
+    finally:
+        c1.close()
+        c2.close()
+
+
+@pytest.mark.parametrize("two_stream", [False, True])
+def test_graph_capture_replays(dev, two_stream):
+    """The step captured into a HIP graph: every replay, with fresh inputs written
+    eagerly between replays, matches an eager run of the same step."""
+    P, B, S_l, H, D = 4, 1, 128, 8, 128
+    qkv = synth.normal((P, B, S_l, 3, H, D), "bf16", 95, dev)
+    o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 96, dev)
+    w_q, w_k = synth.norm_weight(D, "bf16", 97, dev), synth.norm_weight(D, "bf16", 98, dev)
+    cos, sin = (t.to(dev) for t in rope_table_1d(P * S_l, D))
+    q_in, k_in, v_in = qkv[:, :, :, 0], qkv[:, :, :, 1], qkv[:, :, :, 2]
+    ctx = UlyssesContext(P, device=0)
+    try:
+        def step(stream=None):
+            if two_stream:
+                ctx.scatter_qkv(v=v_in, stream=stream)
+                outs = ctx.fused_qk_norm_rope_scatter(q_in, k_in, w_q, w_k, cos, sin, stream=stream)
+                outs = (outs[0], outs[1], ctx.target("v", 0, torch.bfloat16, (B, P * S_l, H // P, D)))
+            else:
+                outs = ctx.fused_qk_norm_rope_scatter(q_in, k_in, w_q, w_k, cos, sin, v=v_in, stream=stream)
+            ctx.wait(stream)
+            z = ctx.gather_out(o, stream=stream)
+            return list(outs) + [z]
+
+        cap = torch.cuda.Stream()
+        with torch.cuda.stream(cap):
+            targets = step(cap)              # registers the targets and fills the event pools
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step(cap)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            qkv.copy_(synth.normal(qkv.shape, "bf16", 200 + rep, dev))
+            o.copy_(synth.normal(o.shape, "bf16", 300 + rep, dev))
+            torch.cuda.synchronize()
+            ref = [t.clone() for t in step()]        # eager, on the current stream
+            torch.cuda.synchronize()
+            for t in targets:
+                t.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for t, r in zip(targets, ref):
+                assert torch.equal(t.view(torch.int16), r.view(torch.int16)), "replay %d differs" % rep
+    finally:
+        torch.cuda.synchronize()
+        ctx.close()
