@@ -270,13 +270,14 @@ typedef enum {
     ULY_K_COUNT = 5
 } uly_kernel_kind;
 
-/* kind_mask bit k (1 << uly_kernel_kind) brackets every launch of kind k
- * with HIP events on the stream it runs on (0 turns timing off; each pair
- * of events adds a little latency between kernels, so time only what is
- * needed); uly_profile_read waits for those events and returns the summed
+/* kind_mask bit k (1 << uly_kernel_kind) brackets launches of kind k with
+ * HIP events on the stream they run on: the first launch of each kind and
+ * then one in every `every` (>= 1).  Each pair of events adds a little
+ * latency between kernels, so time only what is needed; 0 turns timing
+ * off.  uly_profile_read waits for those events and returns the summed
  * kernel time (ms) and the number of timed launches of `kind` since the
  * last reset. */
-uly_status uly_profile_enable(uly_ctx *ctx, int kind_mask);
+uly_status uly_profile_enable(uly_ctx *ctx, int kind_mask, int every);
 uly_status uly_profile_read(uly_ctx *ctx, int kind, double *total_ms, int64_t *launches);
 uly_status uly_profile_reset(uly_ctx *ctx);
 

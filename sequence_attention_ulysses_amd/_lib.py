@@ -143,7 +143,7 @@ def load() -> ctypes.CDLL:
         "uly_spatial_trim_concat": [vp, vp, i32, i64, i64, i64, vp, vp],
         "uly_rope_table_1d": [vp, vp, i64, i64, i64, f64],
         "uly_rope_table_3d": [vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, f64],
-        "uly_profile_enable": [vp, i32],
+        "uly_profile_enable": [vp, i32, i32],
         "uly_profile_read": [vp, i32, ctypes.POINTER(f64), P_I64],
         "uly_profile_reset": [vp],
         "uly_get_stats": [vp, ctypes.POINTER(UlyStats)],

@@ -351,8 +351,9 @@ class UlyssesContext:
         return out
 
     # -- measurement --------------------------------------------------------------
-    def profile(self, on: bool = True, kinds=None) -> None:
-        """Bracket launches with timing events: all kinds, or only `kinds` (names of KERNEL_KINDS)."""
+    def profile(self, on: bool = True, kinds=None, every: int = 1) -> None:
+        """Bracket launches with timing events: all kinds, or only `kinds` (names of KERNEL_KINDS);
+        one launch in `every` of each kind is timed."""
         if not on:
             mask = 0
         elif kinds is None:
@@ -361,7 +362,7 @@ class UlyssesContext:
             mask = 0
             for k in kinds:
                 mask |= 1 << _lib.KERNEL_KINDS[k]
-        check(self._lib.uly_profile_enable(self._h(), mask), "uly_profile_enable")
+        check(self._lib.uly_profile_enable(self._h(), mask, int(every)), "uly_profile_enable")
 
     def profile_read(self, kind: str):
         """(summed kernel ms, launches) of one kernel kind since the last reset."""

@@ -114,7 +114,7 @@ void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
 #define ULY_THREADS 256
 #endif
 #ifndef ULY_COPY_UNROLL
-#define ULY_COPY_UNROLL 4
+#define ULY_COPY_UNROLL 1
 #endif
 #ifndef ULY_ROPE_TOKENS
 #define ULY_ROPE_TOKENS 2

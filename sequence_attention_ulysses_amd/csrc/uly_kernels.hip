@@ -66,6 +66,21 @@ __device__ __forceinline__ float4 load_table4(const float *p) {
     return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 
+// Blocks are dispatched to the 8 XCDs of the chip round-robin.  With
+// ULY_XCD_REMAP the logical block index is permuted so that XCD x works
+// through one contiguous range of the grid (a bijection for any grid size).
+__device__ __forceinline__ uint32_t logical_block(uint32_t bid, uint32_t grid) {
+#ifdef ULY_XCD_REMAP
+    constexpr uint32_t kXcds = 8;
+    const uint32_t q = grid / kXcds, r = grid % kXcds;
+    const uint32_t x = bid % kXcds, k = bid / kXcds;
+    return x * q + min(x, r) + k;
+#else
+    (void)grid;
+    return bid;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // Chunk relayout (Ulysses scatter and gather, "Communication Architecture",
 // "Ulysses").  Up to three operands (Q, K, V) share one launch: blocks
@@ -73,7 +88,7 @@ __device__ __forceinline__ float4 load_table4(const float *p) {
 // copies fill the machine together instead of draining one after another.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void relayout_kernel(CopyBatch b) {
-    const uint32_t bid = blockIdx.x;
+    const uint32_t bid = logical_block(blockIdx.x, gridDim.x);
     int pi = 0;
     if (b.n > 1 && bid >= b.p[1].first_block) pi = 1;
     if (b.n > 2 && bid >= b.p[2].first_block) pi = 2;
@@ -195,7 +210,7 @@ __global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_ker
     const uint32_t grp = threadIdx.x / LANES;
     const uint32_t half = a.D / 2;
     const uint32_t R = a.rpt.d;
-    const uint32_t tk0 = blockIdx.x * TU;
+    const uint32_t tk0 = logical_block(blockIdx.x, gridDim.x) * TU;
     const NormRopeOperand &o0 = a.op[0], &o1 = a.op[1], &o2 = a.op[2];
 
     // TILE: the block's tokens, decoded once.

@@ -160,6 +160,8 @@ struct uly_ctx {
     std::vector<Pending> pending;
     std::vector<hipEvent_t> sync_pool;
     int profile_mask = 0;   // bit k: bracket kernels of kind k with timing events
+    int profile_every = 1;  // time one launch in this many of each timed kind
+    int64_t profile_seen[ULY_K_COUNT] = {};
     std::vector<ProfRecord> prof;
     std::vector<hipEvent_t> timing_pool;
     uly_stats stats{};
@@ -255,7 +257,7 @@ uly_status launch(uly_ctx *c, int kind, hipStream_t s, F &&enqueue) {
     (void)hipGetLastError();   // clear a stale error left by someone else's call
     hipEvent_t e0 = nullptr, e1 = nullptr;
     hipError_t err = hipSuccess;
-    const bool timed = (c->profile_mask >> kind) & 1;
+    const bool timed = ((c->profile_mask >> kind) & 1) && (c->profile_seen[kind]++ % c->profile_every == 0);
     if (timed) {
         e0 = take_event(c->timing_pool, hipEventDefault, err);
         if (!e0) return poison(c, err, "hipEventCreate");
@@ -918,10 +920,13 @@ uly_status uly_rope_table_3d(float *cos_out, float *sin_out, int64_t rows, int64
 
 // ---- measurement and test hooks ------------------------------------------------
 
-uly_status uly_profile_enable(uly_ctx *c, int kind_mask) {
+uly_status uly_profile_enable(uly_ctx *c, int kind_mask, int every) {
     uly_status st = ctx_ok(c);
     if (st != ULY_OK) return st;
+    if (every < 1) return fail(ULY_E_INVAL, "every must be >= 1");
     c->profile_mask = kind_mask & ((1 << ULY_K_COUNT) - 1);
+    c->profile_every = every;
+    for (auto &n : c->profile_seen) n = 0;
     return ULY_OK;
 }
 

@@ -504,6 +504,14 @@ def test_profiling_and_stats(dev):
         ctx.profile_reset()
         assert ctx.profile_read("scatter") == (0.0, 0)
         assert ctx.stats()["launches"] == 2
+        # sampled: the first launch of a kind and then one in every 3
+        ctx.profile(True, kinds=["gather"], every=3)
+        for _ in range(7):
+            ctx.gather_out(ys[0])
+        ctx.scatter_qkv(q, k, v)
+        ms, n = ctx.profile_read("gather")
+        assert n == 3 and ms > 0
+        assert ctx.profile_read("scatter") == (0.0, 0)
 
 
 def test_device_fail_stop(dev):

@@ -347,3 +347,12 @@ def test_python_binding_host_only():
         c2.__del__()
         assert any(issubclass(x.category, ResourceWarning) for x in w)
     c2.close()
+
+
+def test_profile_arguments(lib, ctx4):
+    assert lib.uly_profile_enable(ctx4.h, 0x3, 0) == _lib.E_INVAL
+    assert lib.uly_profile_enable(ctx4.h, 0x3, 4) == _lib.OK
+    assert lib.uly_profile_enable(ctx4.h, 0, 1) == _lib.OK
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.uly_profile_read(ctx4.h, 9, ctypes.byref(ms), ctypes.byref(n)) == _lib.E_INVAL
+    assert lib.uly_profile_read(ctx4.h, 1, ctypes.byref(ms), ctypes.byref(n)) == _lib.OK and n.value == 0
