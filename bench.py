@@ -89,6 +89,151 @@ def cpu_baseline(args, inputs, min_seconds: float = 10.0):
                       % (steps, args.bytes_per_step, dt)}
 
 
+# ---------------------------------------------------------------------------
+# Workloads.  Each setup returns the context, the step (and its two-stream
+# form where there is one), the algorithmic bytes of a step (each input
+# element read once, each output element written once, real tokens only),
+# the dominant kernel (kind, bytes per launch, name) and the JSON config.
+# ---------------------------------------------------------------------------
+def setup_video_dit(torch, dev, synth, rope_table_1d, UlyssesContext):
+    w = synth.VIDEO_DIT
+    P, B, S_l, H, D = w.P, w.B, w.S_l, w.Hq, w.D
+    n_tensor = P * B * S_l * H * D * 2
+    qkv = synth.normal((P, B, S_l, 3, H, D), "bf16", 0)
+    w_q, w_k = synth.norm_weight(D, "bf16", 1), synth.norm_weight(D, "bf16", 2)
+    o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 3)
+    cos, sin = rope_table_1d(P * S_l, D, theta=w.theta)
+    g_qkv, g_wq, g_wk, g_o = qkv.to(dev), w_q.to(dev), w_k.to(dev), o.to(dev)
+    g_cos, g_sin = cos.to(dev), sin.to(dev)
+    q_in, k_in, v_in = g_qkv[:, :, :, 0], g_qkv[:, :, :, 1], g_qkv[:, :, :, 2]
+    ctx = UlyssesContext(P, device=0)
+
+    def step():
+        ctx.fused_qk_norm_rope_scatter(q_in, k_in, g_wq, g_wk, g_cos, g_sin, eps=w.eps, v=v_in)
+        ctx.wait()
+        ctx.gather_out(g_o)
+
+    def step_two_stream():
+        ctx.scatter_qkv(v=v_in, tags=(None, None, "v2"))
+        ctx.fused_qk_norm_rope_scatter(q_in, k_in, g_wq, g_wk, g_cos, g_sin, eps=w.eps)
+        ctx.wait()
+        ctx.gather_out(g_o)
+
+    return {"workload": w, "ctx": ctx, "step": step, "step_two_stream": step_two_stream,
+            "bytes_per_step": 3 * 2 * n_tensor + 2 * n_tensor,
+            "dominant": ("norm_rope", 6 * n_tensor,
+                         "norm_rope_kernel<16,bf16> (Q/K RMSNorm+RoPE scatter with V in the same grid)"),
+            "cpu_inputs": (qkv, w_q, w_k, o), "dtype": "bf16",
+            "data": "synthetic N(0,1) activations, N(1,0.1) norm weights, 1-D RoPE theta 1e4 (seeded)",
+            "config": {"workload": w.name, "P": P, "B": B, "S_local": S_l, "S": P * S_l, "H": H, "D": D,
+                       "v_source": "strided from fused QKV [B,S_local,3,H,D]", "parallelism": "ulysses-p4-emulated",
+                       "bytes_per_step": 3 * 2 * n_tensor + 2 * n_tensor}}
+
+
+def setup_wan_long(torch, dev, synth, rope_table_1d, UlyssesContext):
+    from sequence_attention_ulysses_amd import rope_table_3d
+    w = synth.WAN_LONG
+    P, B, S_l, H, D, S = w.P, w.B, w.S_l, w.Hq, w.D, w.S_real
+    _, Hh, Ww = w.grid
+    ctx = UlyssesContext(P, device=0)
+    # global sequences, padded and sharded once (the pad/trim kernels are not in the step)
+    shards = [ctx.seq_pad_shard(synth.normal((B, S, H, D), "bf16", 30 + i, dev), S_l) for i in range(3)]
+    w_q, w_k = synth.norm_weight(D, "bf16", 31, dev), synth.norm_weight(D, "bf16", 32, dev)
+    cos, sin = (t.to(dev) for t in rope_table_3d(P * S_l, D, Hh, Ww, real_rows=S, theta=w.theta))
+    o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 33, dev)
+    real = B * S * H * D * 2
+
+    def step():
+        ctx.fused_qk_norm_rope_scatter(shards[0], shards[1], w_q, w_k, cos, sin, eps=w.eps, v=shards[2])
+        ctx.wait()
+        ctx.gather_out(o)
+
+    return {"workload": w, "ctx": ctx, "step": step, "bytes_per_step": 3 * 2 * real + 2 * real,
+            "dominant": ("norm_rope", 6 * real, "norm_rope_kernel<16,bf16> (3-D RoPE, padded sequence)"),
+            "dtype": "bf16", "data": "synthetic N(0,1) activations, N(1,0.1) norm weights, 3-D RoPE 44/42/42",
+            "config": {"workload": w.name, "P": P, "B": B, "S": S, "S_padded": P * S_l, "H": H, "D": D,
+                       "bytes_per_step": 3 * 2 * real + 2 * real, "bytes_count": "real tokens only"}}
+
+
+def setup_gqa(torch, dev, synth, rope_table_1d, UlyssesContext):
+    w = synth.GQA
+    P, B, S_l, Hq, Hkv, D = w.P, w.B, w.S_l, w.Hq, w.Hkv, w.D
+    q = synth.normal((P, B, S_l, Hq, D), "bf16", 40, dev)
+    k = synth.normal((P, B, S_l, Hkv, D), "bf16", 41, dev)
+    v = synth.normal((P, B, S_l, Hkv, D), "bf16", 42, dev)
+    o = synth.normal((P, B, P * S_l, Hq // P, D), "bf16", 43, dev)
+    ctx = UlyssesContext(P, device=0)
+    nq, nkv = P * B * S_l * Hq * D * 2, P * B * S_l * Hkv * D * 2
+
+    def step():
+        ctx.scatter_qkv(q, k, v)
+        ctx.wait()
+        ctx.gather_out(o)
+
+    return {"workload": w, "ctx": ctx, "step": step, "bytes_per_step": 2 * (nq + 2 * nkv) + 2 * nq,
+            "dominant": ("scatter", 2 * (nq + 2 * nkv), "relayout_kernel (grouped Q/K/V scatter, one launch)"),
+            "dtype": "bf16", "data": "synthetic N(0,1) activations",
+            "config": {"workload": w.name, "P": P, "B": B, "S_local": S_l, "Hq": Hq, "Hkv": Hkv, "D": D,
+                       "bytes_per_step": 2 * (nq + 2 * nkv) + 2 * nq}}
+
+
+def setup_tiny(torch, dev, synth, rope_table_1d, UlyssesContext):
+    w = synth.TINY
+    P, B, S_l, H, D = w.P, w.B, w.S_l, w.Hq, w.D
+    q, k, v = (synth.normal((P, B, S_l, H, D), "f16", 50 + i, dev) for i in range(3))
+    o = synth.normal((P, B, P * S_l, H // P, D), "f16", 53, dev)
+    ctx = UlyssesContext(P, device=0)
+    n = P * B * S_l * H * D * 2
+
+    def step():
+        ctx.scatter_qkv(q, k, v)
+        ctx.wait()
+        ctx.gather_out(o)
+
+    return {"workload": w, "ctx": ctx, "step": step, "bytes_per_step": 3 * 2 * n + 2 * n,
+            "dominant": ("scatter", 6 * n, "relayout_kernel (grouped Q/K/V scatter, one launch)"),
+            "dtype": "f16", "data": "synthetic N(0,1) activations",
+            "config": {"workload": w.name, "P": P, "B": B, "S_local": S_l, "H": H, "D": D,
+                       "bytes_per_step": 3 * 2 * n + 2 * n, "note": "launch-bound"}}
+
+
+def setup_spatial(torch, dev, synth, rope_table_1d, UlyssesContext):
+    from sequence_attention_ulysses_amd import height_split
+    w = synth.SPATIAL
+    full = synth.normal(w.shape, w.dtype, 60, dev)
+    ctx = UlyssesContext(w.P, device=0)
+    lead, (Hh, W) = w.shape[:-2], w.shape[-2:]
+    N = 1
+    for x in lead:
+        N *= x
+    h, hmax = height_split(Hh, w.P)
+    halo_rows = sum(min(w.halo, sum(h[:r])) + min(w.halo, Hh - sum(h[:r + 1])) for r in range(w.P))
+    row = W * 2
+    # split: read every source row once per use (core rows once, halo rows again), write the shards;
+    # gather: read core rows, write the stacked buffer; trim/concat: read core rows, write the full tensor
+    split = N * row * (Hh + halo_rows) + N * row * w.P * (hmax + 2 * w.halo)
+    gather = N * row * Hh + N * row * w.P * hmax
+    trim = N * row * Hh * 2
+
+    def step():
+        sh = ctx.spatial_split_halo(full, halo=w.halo, out=bufs[0])
+        st = ctx.spatial_gather_stacked(sh, Hh, halo=w.halo, out=bufs[1])
+        ctx.spatial_trim_concat(st, Hh, out=bufs[2])
+
+    bufs = [torch.empty((w.P,) + lead + (hmax + 2 * w.halo, W), dtype=full.dtype, device=dev),
+            torch.empty((w.P,) + lead + (hmax, W), dtype=full.dtype, device=dev),
+            torch.empty(w.shape, dtype=full.dtype, device=dev)]
+    return {"workload": w, "ctx": ctx, "step": step, "bytes_per_step": split + gather + trim,
+            "dominant": ("spatial", (split + gather + trim) // 3, "rowmap_kernel (average of the three launches)"),
+            "dtype": "bf16", "data": "synthetic N(0,1) latent",
+            "config": {"workload": w.name, "P": w.P, "shape": list(w.shape), "heights": h, "halo": w.halo,
+                       "bytes_per_step": split + gather + trim, "note": "cache-resident"}}
+
+
+WORKLOADS = {"video_dit": setup_video_dit, "wan_long": setup_wan_long, "gqa": setup_gqa, "tiny": setup_tiny,
+             "spatial": setup_spatial}
+
+
 def calibrate_copy(args, torch, UlyssesContext):
     """A plain copy of a known size through the library's relayout kernel
     (one rank, so the map is the identity): the reference that scales the
@@ -109,6 +254,8 @@ def calibrate_copy(args, torch, UlyssesContext):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default="video_dit", choices=sorted(WORKLOADS),
+                    help="video_dit (the headline, default) or another workload recorded for reference")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -135,36 +282,16 @@ def main():
         calibrate_copy(args, torch, UlyssesContext)
         return
 
-    w = synth.VIDEO_DIT
-    P, B, S_l, H, D = w.P, w.B, w.S_l, w.Hq, w.D
     dev = torch.device("cuda", 0)
-    elem = 2
-    n_tensor = P * B * S_l * H * D * elem
-    args.bytes_per_step = 3 * 2 * n_tensor + 2 * n_tensor          # QKV scatter (r+w) + output gather (r+w)
+    setup = WORKLOADS[args.workload](torch, dev, synth, rope_table_1d, UlyssesContext)
+    w = setup["workload"]
+    ctx = setup["ctx"]
+    step, step_two_stream = setup["step"], setup.get("step_two_stream")
+    args.bytes_per_step = setup["bytes_per_step"]
+    if step_two_stream is None:
+        args.no_two_stream = True
     print("bench: %s on %s, %d warmup + %d timed steps" % (w.name, torch.cuda.get_device_name(0),
                                                          args.warmup, args.steps), file=sys.stderr, flush=True)
-
-    qkv = synth.normal((P, B, S_l, 3, H, D), "bf16", 0)
-    w_q = synth.norm_weight(D, "bf16", 1)
-    w_k = synth.norm_weight(D, "bf16", 2)
-    o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 3)
-    cos, sin = rope_table_1d(P * S_l, D, theta=w.theta)
-    g_qkv, g_wq, g_wk, g_o = qkv.to(dev), w_q.to(dev), w_k.to(dev), o.to(dev)
-    g_cos, g_sin = cos.to(dev), sin.to(dev)
-    q_in, k_in, v_in = g_qkv[:, :, :, 0], g_qkv[:, :, :, 1], g_qkv[:, :, :, 2]
-
-    ctx = UlyssesContext(P, device=0)
-
-    def step():
-        ctx.fused_qk_norm_rope_scatter(q_in, k_in, g_wq, g_wk, g_cos, g_sin, eps=w.eps, v=v_in)
-        ctx.wait()
-        ctx.gather_out(g_o)
-
-    def step_two_stream():
-        ctx.scatter_qkv(v=v_in, tags=(None, None, "v2"))
-        ctx.fused_qk_norm_rope_scatter(q_in, k_in, g_wq, g_wk, g_cos, g_sin, eps=w.eps)
-        ctx.wait()
-        ctx.gather_out(g_o)
 
     def timed(fn, steps):
         torch.cuda.synchronize()
@@ -179,10 +306,11 @@ def main():
         if not args.no_two_stream:
             step_two_stream()
     torch.cuda.synchronize()
+    dom_kind, dom_bytes, dom_name = setup["dominant"]
     if not args.no_profile:
         # time only the dominant kernel, one launch in PROFILE_EVERY: every event pair adds
         # latency between kernels
-        ctx.profile(True, kinds=["norm_rope"], every=PROFILE_EVERY)
+        ctx.profile(True, kinds=[dom_kind], every=PROFILE_EVERY)
         ctx.profile_reset()
     wall = timed(step, args.steps)
     ms_per_step = wall * 1e3 / args.steps
@@ -191,23 +319,19 @@ def main():
     kernels = {}
     roofline = None
     if not args.no_profile:
-        per_launch_bytes = {"norm_rope": 6 * n_tensor}
-        for kind, nbytes in per_launch_bytes.items():
-            ms, n = ctx.profile_read(kind)
-            if n:
-                avg_us = ms * 1e3 / n
-                kernels[kind] = {"timed_launches": n, "launches": args.steps, "avg_us": round(avg_us, 2),
-                                 "bytes_per_launch": nbytes,
-                                 "GB_s": round(nbytes / (avg_us * 1e-6) / 1e9, 1)}
+        ms, n = ctx.profile_read(dom_kind)
+        if n:
+            avg_us = ms * 1e3 / n
+            kernels[dom_kind] = {"timed_launches": n, "launches": args.steps, "avg_us": round(avg_us, 2),
+                                 "bytes_per_launch": dom_bytes, "GB_s": round(dom_bytes / (avg_us * 1e-6) / 1e9, 1)}
         ctx.profile(False)
         ctx.profile_reset()
-        dom = kernels.get("norm_rope")
+        dom = kernels.get(dom_kind)
         if dom:
             achieved = dom["GB_s"]
             roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(w.name),
-                        "kernel": "norm_rope_kernel<16,bf16> (Q/K RMSNorm+RoPE scatter with V in the same grid)",
-                        "algorithmic_bytes_per_launch": dom["bytes_per_launch"], "avg_us": dom["avg_us"]}
+                        "kernel": dom_name, "algorithmic_bytes_per_launch": dom_bytes, "avg_us": dom["avg_us"]}
 
     # the two-stream form of the same step, timed the same way (no events)
     two_stream = None
@@ -236,12 +360,12 @@ def main():
     ctx.close()
 
     cpu = None
-    if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle on one step", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(args, (qkv, w_q, w_k, o))
+    if not args.no_cpu_baseline and "cpu_inputs" in setup:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args, setup["cpu_inputs"])
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "video_dit" else "Ulysses exchange GB/s, workload %s" % w.name,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -251,11 +375,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic N(0,1) activations, N(1,0.1) norm weights, 1-D RoPE theta 1e4 (seeded)",
-        "config": {"workload": w.name, "P": P, "B": B, "S_local": S_l, "S": P * S_l, "H": H, "D": D,
-                   "v_source": "strided from fused QKV [B,S_local,3,H,D]", "parallelism": "ulysses-p4-emulated",
-                   "bytes_per_step": args.bytes_per_step},
+        "dtype": setup["dtype"],
+        "data": setup["data"],
+        "config": setup["config"],
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": roofline,
         "kernels": kernels,
