@@ -36,7 +36,8 @@ def build(force: bool = True) -> str:
     """Compile ``uly_oracle.c`` with the host C compiler into ``liboracle.so``."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wl,-soname,liboracle.so",
+                               "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 

@@ -621,3 +621,59 @@ def test_graph_capture_replays(dev, two_stream):
     finally:
         torch.cuda.synchronize()
         ctx.close()
+
+
+def _random_case(rng):
+    P = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    D = int(rng.choice([32, 64, 128, 256]))
+    Hl_q = int(rng.integers(1, 5))
+    Hl_k = int(rng.integers(1, Hl_q + 1))
+    B = int(rng.integers(1, 3))
+    S_l = int(rng.integers(1, 97))
+    dtype = str(rng.choice(["bf16", "f16"]))
+    pad = int(rng.choice([0, 8, 64]))          # extra elements per token row: a strided source
+    return P, B, S_l, P * Hl_q, P * Hl_k, D, dtype, pad
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_all_paths(dev, orc, seed):
+    """Random world sizes, head counts, head dims, tails, dtypes and source row
+    padding through the plain scatter, the fused norm + RoPE scatter (with V) and
+    the gather, each against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    P, B, S_l, Hq, Hk, D, dtype, pad = _random_case(rng)
+    print("case P=%d B=%d S_l=%d Hq=%d Hk=%d D=%d %s pad=%d" % (P, B, S_l, Hq, Hk, D, dtype, pad), flush=True)
+    row = (Hq + 2 * Hk) * D + pad
+    base = synth.normal((P, B, S_l, row), dtype, 2000 + seed, dev)
+    q = base[..., :Hq * D].unflatten(-1, (Hq, D))
+    k = base[..., Hq * D:(Hq + Hk) * D].unflatten(-1, (Hk, D))
+    v = base[..., (Hq + Hk) * D:(Hq + 2 * Hk) * D].unflatten(-1, (Hk, D))
+    w_q, w_k = synth.norm_weight(D, dtype, 3000 + seed, dev), synth.norm_weight(D, dtype, 4000 + seed, dev)
+    rows = P * S_l + int(rng.integers(0, 4))
+    cos, sin = rope_table_1d(rows, D)
+    ocos, osin = orc.rope_table_1d(rows, D)
+    with UlyssesContext(P, device=0) as ctx:
+        ys = ctx.scatter_qkv(q, k, v, tags=("pq", "pk", "pv"))
+        yq, yk, yv = ctx.fused_qk_norm_rope_scatter(q, k, w_q, w_k, cos.to(dev), sin.to(dev), v=v)
+        ctx.wait()
+        z = ctx.gather_out(ys[0], tag="z")
+        torch.cuda.synchronize()
+        for x, y in zip((q, k, v), ys):
+            np.testing.assert_array_equal(to_bits(y), orc.scatter(to_bits(x.contiguous())))
+        np.testing.assert_array_equal(to_bits(yv), orc.scatter(to_bits(v.contiguous())))
+        assert torch.equal(z.view(torch.int16), q.contiguous().view(torch.int16))
+        for x, w, y, name in ((q, w_q, yq, "q"), (k, w_k, yk, "k")):
+            ref = orc.fused_norm_rope_scatter(to_bits(x.contiguous()), dtype, to_bits(w), 1e-6, ocos, osin)
+            assert_close16(y, ref, dtype, name)
+
+
+def test_c_program_uses_the_abi_alone(dev):
+    """A C program linked against libuly.so (built by __graft_entry__.build()) runs the
+    scatter and gather through include/uly.h and checks them against the oracle."""
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(__file__), "c_abi", "uly_c_smoke")
+    assert os.path.exists(exe), "tests/c_abi/uly_c_smoke is not built; run __graft_entry__.build()"
+    torch.cuda.synchronize()
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout + out.stderr
