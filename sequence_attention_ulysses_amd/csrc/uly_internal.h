@@ -119,13 +119,17 @@ void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
 #ifndef ULY_ROPE_TOKENS
 #define ULY_ROPE_TOKENS 2
 #endif
+#ifndef ULY_ROPE_SLOTS
+#define ULY_ROPE_SLOTS 2
+#endif
 #ifndef ULY_ROPE_THREADS
 #define ULY_ROPE_THREADS 512
 #endif
 constexpr int kThreads = ULY_THREADS;
 constexpr int kCopyUnroll = ULY_COPY_UNROLL;             // 16-byte vectors per thread
 constexpr uint32_t kCopyVecsPerBlock = kThreads * kCopyUnroll;
-constexpr int kRopeTokens = ULY_ROPE_TOKENS;            // tokens per block (rows in flight per group)
+constexpr int kRopeTokens = ULY_ROPE_TOKENS;            // tokens per block
+constexpr int kRopeSlots = ULY_ROPE_SLOTS;              // head slots a lane group loads at once
 constexpr int kRopeThreads = ULY_ROPE_THREADS;          // threads per block of the fused kernel
 
 }  // namespace uly

@@ -202,119 +202,146 @@ __device__ __forceinline__ T sel3(uint32_t i, T a, T b, T c) {
 #define ULY_ROPE_OCCUPANCY
 #endif
 
+// One head slot of a lane group: where its rows come from and go to.
+template <int DT>
+struct Slot {
+    const uint16_t *src;   // this lane's 8 elements of the head, token offsets still to add
+    uint16_t *dst;
+    int64_t s_rank, s_b, s_s, d_b, d_g;
+    float w[8];
+    bool rope;             // Q or K (normalised and rotated); V is copied
+    bool live;             // the slot exists (the last slots of a group may not)
+};
+
+template <int DT, bool UNI>
+__device__ __forceinline__ Slot<DT> make_slot(const NormRopeArgs &a, uint32_t hh, uint32_t R, uint32_t lane) {
+    const NormRopeOperand &o0 = a.op[0], &o1 = a.op[1], &o2 = a.op[2];
+    Slot<DT> sl;
+    sl.live = hh < R;
+    const uint32_t hc = sl.live ? hh : R - 1;                  // dead slots read a valid row
+    const uint32_t hh_op = UNI ? __builtin_amdgcn_readfirstlane(hc) : hc;
+    const uint32_t oi = (hh_op >= a.H0 ? 1u : 0u) + (hh_op >= a.H01 ? 1u : 0u);
+    const uint32_t h = hc - sel3(oi, 0u, a.H0, a.H01);
+    uint32_t qd, j;
+    if (oi == 0) o0.hl.divmod(h, qd, j);
+    else if (oi == 1) o1.hl.divmod(h, qd, j);
+    else o2.hl.divmod(h, qd, j);
+    sl.s_rank = sel3(oi, o0.s_rank, o1.s_rank, o2.s_rank);
+    sl.s_b = sel3(oi, o0.s_b, o1.s_b, o2.s_b);
+    sl.s_s = sel3(oi, o0.s_s, o1.s_s, o2.s_s);
+    sl.d_b = sel3(oi, o0.d_b, o1.d_b, o2.d_b);
+    sl.d_g = sel3(oi, o0.d_g, o1.d_g, o2.d_g);
+    sl.src = sel3(oi, o0.src, o1.src, o2.src) + int64_t(h) * sel3(oi, o0.s_h, o1.s_h, o2.s_h) + lane * 8;
+    sl.dst = sel3(oi, o0.dst, o1.dst, o2.dst) + int64_t(qd) * sel3(oi, o0.d_q, o1.d_q, o2.d_q) +
+             int64_t(j) * a.D + lane * 8;
+    sl.rope = oi < 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sl.w[i] = 0.f;
+    if (sl.rope) unpack8<DT>(load16_cached(sel3(oi, o0.w, o1.w, o2.w) + lane * 8), sl.w);
+    return sl;
+}
+
+// Work mapping.  A block owns a tile of kRopeTokens consecutive tokens
+// (source order r, b, s).  Its GROUPS lane groups split the R = H0+H1+H2
+// rows of a token: group gi owns the row slots hh = gi, gi + GROUPS, ...,
+// the same for every token, and loads kRopeSlots of them at once.  The
+// per-head part of the addressing is computed once per slot; the token
+// part (r, b, s, g, the table row) once per block.
+//   UNI:  every operand's head count is a multiple of the groups per wave,
+//         so a wave's slots never straddle two operands: the operand of a
+//         slot is wave-uniform and every per-operand field is a scalar.
+//   TILE: S_l is a multiple of the tile, so a tile never crosses a rank or
+//         batch boundary: one decode per block, token t of the tile is
+//         s0 + t at global position g0 + t, and there is no partial tile.
+// Rows of operand 2 (V) ride in the same grid as plain 16-byte copies: the
+// whole Q/K/V scatter is one launch that shares HBM bandwidth without a
+// second kernel's ramp-up and tail.
 template <int LANES, int DT, bool UNI, bool TILE>
 __global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_kernel(NormRopeArgs a) {
     constexpr int GROUPS = kRopeThreads / LANES;
     constexpr int TU = kRopeTokens;
+    constexpr int SU = kRopeSlots;
     const uint32_t lane = threadIdx.x % LANES;
     const uint32_t grp = threadIdx.x / LANES;
     const uint32_t half = a.D / 2;
     const uint32_t R = a.rpt.d;
     const uint32_t tk0 = logical_block(blockIdx.x, gridDim.x) * TU;
-    const NormRopeOperand &o0 = a.op[0], &o1 = a.op[1], &o2 = a.op[2];
 
-    // TILE: the block's tokens, decoded once.
-    uint32_t r0 = 0, b0 = 0, s0 = 0, g0 = 0;
-    if (TILE) {
-        uint32_t rb;
-        a.sl.divmod(tk0, rb, s0);
-        a.bdiv.divmod(rb, r0, b0);
-        g0 = r0 * a.S_l + s0;
+    // Token part, once per block: (r, b, s, g) of each token and its table row.
+    uint32_t tr[TU], tb[TU], ts[TU];
+    bool live[TU];
+    float4 cs[TU], sn[TU];
+#pragma unroll
+    for (int t = 0; t < TU; ++t) {
+        uint32_t rb, g;
+        if (TILE) {
+            if (t == 0) {
+                a.sl.divmod(tk0, rb, ts[0]);
+                a.bdiv.divmod(rb, tr[0], tb[0]);
+            } else {
+                tr[t] = tr[0];
+                tb[t] = tb[0];
+                ts[t] = ts[0] + t;
+            }
+            live[t] = true;
+        } else {
+            live[t] = tk0 + t < a.tokens;          // uniform across the block
+            const uint32_t tk = live[t] ? tk0 + t : a.tokens - 1;
+            a.sl.divmod(tk, rb, ts[t]);
+            a.bdiv.divmod(rb, tr[t], tb[t]);
+        }
+        g = tr[t] * a.S_l + ts[t];
+        cs[t] = make_float4(1.f, 1.f, 1.f, 1.f);
+        sn[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (a.H01 > 0) {
+            const size_t t_off = size_t(g) * half + lane * 4;
+            cs[t] = load_table4(a.cos_tab + t_off);
+            sn[t] = load_table4(a.sin_tab + t_off);
+        }
     }
 
-    // Every lane of a group runs the same slot and token trips; tokens past
-    // the end (only without TILE) are computed on a clamped row and not
-    // stored, so every lane of a group takes part in every DPP exchange.
-    for (uint32_t hh = grp; hh < R; hh += GROUPS) {
-        // per-slot (per-head) part
-        const uint32_t hh_op = UNI ? __builtin_amdgcn_readfirstlane(hh) : hh;
-        const uint32_t oi = (hh_op >= a.H0 ? 1u : 0u) + (hh_op >= a.H01 ? 1u : 0u);
-        const uint32_t h = hh - sel3(oi, 0u, a.H0, a.H01);
-        uint32_t qd, j;
-        if (oi == 0) o0.hl.divmod(h, qd, j);
-        else if (oi == 1) o1.hl.divmod(h, qd, j);
-        else o2.hl.divmod(h, qd, j);
-        const int64_t s_rank = sel3(oi, o0.s_rank, o1.s_rank, o2.s_rank);
-        const int64_t s_b = sel3(oi, o0.s_b, o1.s_b, o2.s_b);
-        const int64_t s_s = sel3(oi, o0.s_s, o1.s_s, o2.s_s);
-        const int64_t d_b = sel3(oi, o0.d_b, o1.d_b, o2.d_b);
-        const int64_t d_g = sel3(oi, o0.d_g, o1.d_g, o2.d_g);
-        const uint16_t *src_h = sel3(oi, o0.src, o1.src, o2.src) +
-                                int64_t(h) * sel3(oi, o0.s_h, o1.s_h, o2.s_h) + lane * 8;
-        uint16_t *dst_h = sel3(oi, o0.dst, o1.dst, o2.dst) +
-                          int64_t(qd) * sel3(oi, o0.d_q, o1.d_q, o2.d_q) + int64_t(j) * a.D + lane * 8;
-        const bool rope = oi < 2;
-        float w[8];
+    // Every lane of a group runs the same slot and token trips; dead slots
+    // and tokens past the end are computed on a valid row and not stored, so
+    // every lane of a group takes part in every DPP exchange.
+    for (uint32_t hh = grp; hh < R; hh += GROUPS * SU) {
+        Slot<DT> sl[SU];
+        uint4 raw[SU][TU];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = 0.f;
-        if (rope) unpack8<DT>(load16_cached(sel3(oi, o0.w, o1.w, o2.w) + lane * 8), w);
-
-        uint4 raw[TU];
-        float4 cs[TU], sn[TU];
-        int64_t doff[TU];
-        bool live[TU];
-        if (TILE) {
-            const uint16_t *src_t = src_h + (int64_t(r0) * s_rank + int64_t(b0) * s_b + int64_t(s0) * s_s);
-            const int64_t d0 = int64_t(b0) * d_b + int64_t(g0) * d_g;
+        for (int u = 0; u < SU; ++u) {
+            sl[u] = make_slot<DT, UNI>(a, hh + u * GROUPS, R, lane);
 #pragma unroll
-            for (int t = 0; t < TU; ++t) {
-                live[t] = true;
-                raw[t] = load16(src_t + t * s_s);
-                doff[t] = d0 + t * d_g;
-            }
-#pragma unroll
-            for (int t = 0; t < TU; ++t) {
-                cs[t] = make_float4(1.f, 1.f, 1.f, 1.f);
-                sn[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (rope) {
-                    const size_t t_off = size_t(g0 + t) * half + lane * 4;
-                    cs[t] = load_table4(a.cos_tab + t_off);
-                    sn[t] = load_table4(a.sin_tab + t_off);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < TU; ++t) {
-                live[t] = tk0 + t < a.tokens;      // uniform across the block
-                const uint32_t tk = live[t] ? tk0 + t : a.tokens - 1;
-                uint32_t rb, s, r, b;
-                a.sl.divmod(tk, rb, s);
-                a.bdiv.divmod(rb, r, b);
-                const uint32_t g = r * a.S_l + s;
-                raw[t] = load16(src_h + (int64_t(r) * s_rank + int64_t(b) * s_b + int64_t(s) * s_s));
-                doff[t] = int64_t(b) * d_b + int64_t(g) * d_g;
-                cs[t] = make_float4(1.f, 1.f, 1.f, 1.f);
-                sn[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (rope) {
-                    const size_t t_off = size_t(g) * half + lane * 4;
-                    cs[t] = load_table4(a.cos_tab + t_off);
-                    sn[t] = load_table4(a.sin_tab + t_off);
-                }
-            }
+            for (int t = 0; t < TU; ++t)
+                raw[u][t] = load16(sl[u].src + (int64_t(tr[t]) * sl[u].s_rank + int64_t(tb[t]) * sl[u].s_b +
+                                                int64_t(ts[t]) * sl[u].s_s));
         }
 #pragma unroll
-        for (int t = 0; t < TU; ++t) {
-            float x[8];
-            unpack8<DT>(raw[t], x);
-            float ss = 0.f;
+        for (int u = 0; u < SU; ++u) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
-            ss = row_sum<LANES>(ss);
-            // eps > 0 keeps the argument normal: the bare reciprocal square root suffices
-            const float inv = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_D, a.eps));
-            const float c[4] = {cs[t].x, cs[t].y, cs[t].z, cs[t].w};
-            const float sv[4] = {sn[t].x, sn[t].y, sn[t].z, sn[t].w};
-            uint32_t out[4];
+            for (int t = 0; t < TU; ++t) {
+                float x[8];
+                unpack8<DT>(raw[u][t], x);
+                float ss = 0.f;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const float n0 = x[2 * p] * inv * w[2 * p];
-                const float n1 = x[2 * p + 1] * inv * w[2 * p + 1];
-                const float y0 = n0 * c[p] - n1 * sv[p];
-                const float y1 = n0 * sv[p] + n1 * c[p];
-                out[p] = pack2<DT>(y0, y1);
+                for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+                ss = row_sum<LANES>(ss);
+                // eps > 0 keeps the argument normal: the bare reciprocal square root suffices
+                const float inv = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_D, a.eps));
+                const float c[4] = {cs[t].x, cs[t].y, cs[t].z, cs[t].w};
+                const float sv[4] = {sn[t].x, sn[t].y, sn[t].z, sn[t].w};
+                uint32_t out[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float n0 = x[2 * p] * inv * sl[u].w[2 * p];
+                    const float n1 = x[2 * p + 1] * inv * sl[u].w[2 * p + 1];
+                    const float y0 = n0 * c[p] - n1 * sv[p];
+                    const float y1 = n0 * sv[p] + n1 * c[p];
+                    out[p] = pack2<DT>(y0, y1);
+                }
+                const uint4 res = sl[u].rope ? make_uint4(out[0], out[1], out[2], out[3]) : raw[u][t];
+                const uint32_t g = tr[t] * a.S_l + ts[t];
+                if (sl[u].live && live[t])
+                    store16(sl[u].dst + (int64_t(tb[t]) * sl[u].d_b + int64_t(g) * sl[u].d_g), res);
             }
-            const uint4 res = rope ? make_uint4(out[0], out[1], out[2], out[3]) : raw[t];  // V: unchanged
-            if (live[t]) store16(dst_h + doff[t], res);
         }
     }
 }
