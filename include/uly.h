@@ -293,6 +293,16 @@ uly_status uly_get_stats(uly_ctx *ctx, uly_stats *out);
 /* The context's comm stream (for callers that want to order against it). */
 uly_status uly_comm_stream(uly_ctx *ctx, hipStream_t *out);
 
+/* How ulysses_scatter_qkv moves its operands.  ULY_ROUTE_KERNEL (default):
+ * one relayout kernel on the compute units.  ULY_ROUTE_COPY_ENGINE: one
+ * 2-D copy per (source rank, destination rank, batch) block on the copy
+ * engines, straight into the final layout, leaving the compute units to the
+ * fused Q/K kernel ([P27 "Description": copy-engine transfers overlapping
+ * Q/K preprocessing]).  Head bands of more than one head must be packed
+ * (stride[2] == D), as for the kernel route. */
+typedef enum { ULY_ROUTE_KERNEL = 0, ULY_ROUTE_COPY_ENGINE = 1 } uly_route;
+uly_status uly_set_route(uly_ctx *ctx, int route);
+
 /* Fault injection for tests of the fail-stop rule: the `after`-th next
  * launch (0 = the next one) is not enqueued and reports a HIP failure. */
 uly_status uly_debug_fail_launch(uly_ctx *ctx, int after);

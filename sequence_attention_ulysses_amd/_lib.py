@@ -31,6 +31,8 @@ F16 = 1
 BF16 = 2
 MODE_SCATTER = 0
 MODE_GATHER = 1
+ROUTE_KERNEL = 0
+ROUTE_COPY_ENGINE = 1
 
 K_SCATTER, K_NORM_ROPE, K_GATHER, K_PAD, K_SPATIAL = range(5)
 KERNEL_KINDS = {"scatter": K_SCATTER, "norm_rope": K_NORM_ROPE, "gather": K_GATHER,
@@ -43,7 +45,7 @@ EXPORTS = (
     "uly_seq_pad_shard", "uly_seq_unshard_trim", "uly_spatial_split_halo",
     "uly_spatial_gather_stacked", "uly_spatial_trim_concat", "uly_rope_table_1d",
     "uly_rope_table_3d", "uly_profile_enable", "uly_profile_read", "uly_profile_reset",
-    "uly_get_stats", "uly_comm_stream", "uly_debug_fail_launch", "uly_last_error",
+    "uly_get_stats", "uly_comm_stream", "uly_set_route", "uly_debug_fail_launch", "uly_last_error",
     "uly_status_string",
 )
 
@@ -148,6 +150,7 @@ def load() -> ctypes.CDLL:
         "uly_profile_reset": [vp],
         "uly_get_stats": [vp, ctypes.POINTER(UlyStats)],
         "uly_comm_stream": [vp, ctypes.POINTER(vp)],
+        "uly_set_route": [vp, i32],
         "uly_debug_fail_launch": [vp, i32],
     }
     for name, argtypes in sig.items():

@@ -390,5 +390,10 @@ class UlyssesContext:
         check(self._lib.uly_comm_stream(self._h(), ctypes.byref(h)), "uly_comm_stream")
         return h.value or 0
 
+    def set_route(self, route: str) -> None:
+        """How scatter_qkv moves its operands: "kernel" (compute units) or "copy_engine"."""
+        code = {"kernel": _lib.ROUTE_KERNEL, "copy_engine": _lib.ROUTE_COPY_ENGINE}[route]
+        check(self._lib.uly_set_route(self._h(), code), "uly_set_route")
+
     def debug_fail_launch(self, after: int = 0) -> None:
         check(self._lib.uly_debug_fail_launch(self._h(), int(after)), "uly_debug_fail_launch")

@@ -125,6 +125,23 @@ void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
 #ifndef ULY_ROPE_THREADS
 #define ULY_ROPE_THREADS 512
 #endif
+#ifndef ULY_RELAYOUT_NT_LOAD
+#define ULY_RELAYOUT_NT_LOAD 1
+#endif
+#ifndef ULY_RELAYOUT_NT_STORE
+#define ULY_RELAYOUT_NT_STORE 1
+#endif
+#ifndef ULY_ROPE_NT_LOAD
+#define ULY_ROPE_NT_LOAD 1
+#endif
+#ifndef ULY_ROPE_NT_STORE
+#define ULY_ROPE_NT_STORE 1
+#endif
+// Non-temporal (streaming) policy of the operand loads and stores per kernel.
+constexpr bool kRelayoutNtLoad = ULY_RELAYOUT_NT_LOAD;
+constexpr bool kRelayoutNtStore = ULY_RELAYOUT_NT_STORE;
+constexpr bool kRopeNtLoad = ULY_ROPE_NT_LOAD;
+constexpr bool kRopeNtStore = ULY_ROPE_NT_STORE;
 constexpr int kThreads = ULY_THREADS;
 constexpr int kCopyUnroll = ULY_COPY_UNROLL;             // 16-byte vectors per thread
 constexpr uint32_t kCopyVecsPerBlock = kThreads * kCopyUnroll;

@@ -30,27 +30,24 @@ typedef __attribute__((address_space(1))) u32x4 global_u32x4;
 
 // All operands live in device (global) memory: the explicit address space
 // keeps the accesses global_load/store instead of flat ones.  Operand data
-// streams through exactly once, so its 16-byte accesses are non-temporal
-// (they do not displace lines that are reused); building with
-// ULY_TEMPORAL_STREAMS turns that off.
+// streams through exactly once, so by default its 16-byte accesses are
+// non-temporal (they do not displace lines that are reused); each kernel
+// picks the policy of its loads and of its stores (uly_internal.h).
+template <bool NT>
 __device__ __forceinline__ uint4 load16(const void *p) {
     const global_u32x4 *g = (const global_u32x4 *)p;
-#ifndef ULY_TEMPORAL_STREAMS
-    const u32x4 v = __builtin_nontemporal_load(g);
-#else
-    const u32x4 v = *g;
-#endif
+    u32x4 v;
+    if constexpr (NT) v = __builtin_nontemporal_load(g);
+    else v = *g;
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+template <bool NT>
 __device__ __forceinline__ void store16(void *p, uint4 v) {
     global_u32x4 *g = (global_u32x4 *)p;
     const u32x4 w = {v.x, v.y, v.z, v.w};
-#ifndef ULY_TEMPORAL_STREAMS
-    __builtin_nontemporal_store(w, g);
-#else
-    *g = w;
-#endif
+    if constexpr (NT) __builtin_nontemporal_store(w, g);
+    else *g = w;
 }
 
 // Data every block re-reads (norm weights): ordinary cached load.
@@ -110,13 +107,13 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(CopyBatch b) {
                                int64_t(i2) * P.ss[2] + int64_t(i3) * P.ss[3] + uint64_t(c) * 16u;
             d[u] = P.dst + int64_t(i0) * P.ds[0] + int64_t(i1) * P.ds[1] + int64_t(i2) * P.ds[2] +
                    int64_t(i3) * P.ds[3] + uint64_t(c) * 16u;
-            v[u] = load16(s);
+            v[u] = load16<kRelayoutNtLoad>(s);
         }
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
         const uint32_t i = first + u * kThreads;
-        if (i < P.total) store16(d[u], v[u]);
+        if (i < P.total) store16<kRelayoutNtStore>(d[u], v[u]);
     }
 }
 
@@ -311,7 +308,7 @@ __global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_ker
             sl[u] = make_slot<DT, UNI>(a, hh + u * GROUPS, R, lane);
 #pragma unroll
             for (int t = 0; t < TU; ++t)
-                raw[u][t] = load16(sl[u].src + (int64_t(tr[t]) * sl[u].s_rank + int64_t(tb[t]) * sl[u].s_b +
+                raw[u][t] = load16<kRopeNtLoad>(sl[u].src + (int64_t(tr[t]) * sl[u].s_rank + int64_t(tb[t]) * sl[u].s_b +
                                                 int64_t(ts[t]) * sl[u].s_s));
         }
 #pragma unroll
@@ -340,7 +337,7 @@ __global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_ker
                 const uint4 res = sl[u].rope ? make_uint4(out[0], out[1], out[2], out[3]) : raw[u][t];
                 const uint32_t g = tr[t] * a.S_l + ts[t];
                 if (sl[u].live && live[t])
-                    store16(sl[u].dst + (int64_t(tb[t]) * sl[u].d_b + int64_t(g) * sl[u].d_g), res);
+                    store16<kRopeNtStore>(sl[u].dst + (int64_t(tb[t]) * sl[u].d_b + int64_t(g) * sl[u].d_g), res);
             }
         }
     }
@@ -407,13 +404,13 @@ __global__ __launch_bounds__(kThreads) void rowmap_kernel(RowMapArgs a) {
             uint32_t row, c;
             a.vpr.divmod(i, row, c);
             const int64_t src_row = rowmap_source<KIND>(a, row);
-            if (src_row >= 0) v[u] = load16(a.src + (src_row * a.vpr.d + c) * 16);
+            if (src_row >= 0) v[u] = load16<kRelayoutNtLoad>(a.src + (src_row * a.vpr.d + c) * 16);
         }
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
         const uint32_t i = first + u * kThreads;
-        if (i < a.total) store16(a.dst + uint64_t(i) * 16u, v[u]);
+        if (i < a.total) store16<kRelayoutNtStore>(a.dst + uint64_t(i) * 16u, v[u]);
     }
 }
 

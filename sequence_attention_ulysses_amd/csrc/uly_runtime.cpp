@@ -166,6 +166,7 @@ struct uly_ctx {
     std::vector<hipEvent_t> timing_pool;
     uly_stats stats{};
     int fail_after = -1;
+    int route = ULY_ROUTE_KERNEL;   // how ulysses_scatter_qkv moves its operands
 };
 
 namespace {
@@ -367,6 +368,24 @@ uly_status plan_gather(const Operand &o, int P, uint8_t *dst, CopyPlan &p) {
     return ULY_OK;
 }
 
+// Copy-engine form of one scatter member: block (r, q, b) is S_l rows of
+// Hl*D elements at the source token pitch, landing as one dense run in the
+// destination [P(q)][B][S][Hl][D].
+hipError_t copy_engine_scatter(const Operand &x, int P, uint8_t *dst, hipStream_t s) {
+    const int64_t Hl = x.H / P, S = int64_t(P) * x.S, C = Hl * x.D * 2;
+    for (int64_t r = 0; r < P; ++r)
+        for (int64_t q = 0; q < P; ++q)
+            for (int64_t b = 0; b < x.B; ++b) {
+                const uint8_t *src = x.data + 2 * (r * x.rank_stride + b * x.sb + q * Hl * x.sh);
+                uint8_t *d = dst + ((q * x.B + b) * S + r * x.S) * C;
+                const size_t pitch = x.S > 1 ? size_t(x.ss * 2) : size_t(C);
+                hipError_t e = hipMemcpy2DAsync(d, size_t(C), src, pitch, size_t(C), size_t(x.S),
+                                                hipMemcpyDeviceToDeviceNoCU, s);
+                if (e != hipSuccess) return e;
+            }
+    return hipSuccess;
+}
+
 uly_status finish_batch(CopyBatch &b) {
     uint64_t blocks = 0;
     for (int i = 0; i < b.n; ++i) {
@@ -532,6 +551,7 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
     const uly_tensor *mem[3] = {q, k, v};
     const char *names[3] = {"q", "k", "v"};
     Operand ops[3];
+    uint8_t *dsts[3] = {nullptr, nullptr, nullptr};
     int present = 0, dtype = 0;
     int64_t B = -1, S = -1, D = -1;
     std::vector<Range> in_ranges, out_ranges;
@@ -561,6 +581,7 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
         if ((st = resolve_target(c, names[i], tags ? tags[i] : nullptr, outs ? outs[i] : nullptr,
                                  ULY_MODE_SCATTER, x.dtype, tshape, dst)) != ULY_OK)
             return st;
+        dsts[i] = dst;
         in_ranges.push_back(x.range);
         out_ranges.push_back(dense_range(dst, int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3]));
         if ((st = plan_scatter(x, c->P, dst, batch.p[batch.n])) != ULY_OK) return st;
@@ -573,7 +594,26 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
     if (batch.n == 0) return ULY_OK;
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
+    if (c->route == ULY_ROUTE_COPY_ENGINE)
+        for (int i = 0; i < 3; ++i)
+            if (mem[i] && !ops[i].empty() && ops[i].S > 1 && ops[i].ss * 2 < (ops[i].H / c->P) * ops[i].D * 2)
+                return fail(ULY_E_UNSUPPORTED, "%s: copy engines need a token pitch of at least one head band",
+                            names[i]);
     if ((st = fork_comm(c, caller)) != ULY_OK) return st;
+    if (c->route == ULY_ROUTE_COPY_ENGINE) {
+        // One 2-D copy per (source rank, destination rank, batch) block, straight
+        // into the final layout, on the copy engines instead of the compute units.
+        hipError_t cerr = hipSuccess;
+        st = launch(c, ULY_K_SCATTER, c->comm, [&] {
+            for (int i = 0; i < 3 && cerr == hipSuccess; ++i) {
+                if (!mem[i] || ops[i].empty()) continue;
+                cerr = copy_engine_scatter(ops[i], c->P, dsts[i], c->comm);
+            }
+        });
+        if (st != ULY_OK) return st;
+        if (cerr != hipSuccess) return poison(c, cerr, "hipMemcpy2DAsync");
+        return mark_pending(c, c->comm);
+    }
     if ((st = launch(c, ULY_K_SCATTER, c->comm, [&] { launch_relayout(batch, c->comm); })) != ULY_OK)
         return st;
     return mark_pending(c, c->comm);
@@ -974,6 +1014,14 @@ uly_status uly_get_stats(uly_ctx *c, uly_stats *out) {
 uly_status uly_comm_stream(uly_ctx *c, hipStream_t *out) {
     if (!c || !out) return fail(ULY_E_INVAL, "null argument");
     *out = c->comm;
+    return ULY_OK;
+}
+
+uly_status uly_set_route(uly_ctx *c, int route) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    if (route != ULY_ROUTE_KERNEL && route != ULY_ROUTE_COPY_ENGINE) return fail(ULY_E_INVAL, "bad route %d", route);
+    c->route = route;
     return ULY_OK;
 }
 

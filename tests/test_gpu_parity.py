@@ -677,3 +677,27 @@ def test_c_program_uses_the_abi_alone(dev):
     torch.cuda.synchronize()
     out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout + out.stderr
+
+
+@pytest.mark.parametrize("P,B,S_l,Hq,Hkv,D,fused", [(4, 1, 4096, 24, 24, 128, True), (8, 2, 33, 32, 8, 128, False),
+                                                    (1, 1, 17, 4, 4, 64, False), (2, 1, 1, 8, 8, 64, False)])
+def test_copy_engine_route(dev, orc, P, B, S_l, Hq, Hkv, D, fused):
+    """The copy-engine route moves the same bits as the kernel route."""
+    if fused:
+        qkv = synth.normal((P, B, S_l, 3, Hq, D), "bf16", 110, dev)
+        q, k, v = qkv[:, :, :, 0], qkv[:, :, :, 1], qkv[:, :, :, 2]
+    else:
+        q, k, v = contiguous_qkv(P, B, S_l, Hq, D, "bf16", 111, dev, Hkv)
+    with UlyssesContext(P, device=0) as ctx:
+        ctx.set_route("copy_engine")
+        ys = ctx.scatter_qkv(q, k, v)
+        ctx.wait()
+        torch.cuda.synchronize()
+        for x, y in zip((q, k, v), ys):
+            np.testing.assert_array_equal(to_bits(y), orc.scatter(to_bits(x.contiguous())))
+        ctx.set_route("kernel")
+        ys2 = ctx.scatter_qkv(q, k, v, tags=("q2", "k2", "v2"))
+        ctx.wait()
+        torch.cuda.synchronize()
+        for y, y2 in zip(ys, ys2):
+            assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
