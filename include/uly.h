@@ -45,7 +45,8 @@
  *
  * Alignment.  Every device pointer and every byte stride of a copied or
  *   normalised row must be a multiple of 16 bytes (rows move as 16-byte
- *   vectors); in particular D * element_size % 16 == 0.
+ *   vectors); in particular D * element_size % 16 == 0 (element size 2 for
+ *   ULY_F16 / ULY_BF16, 1 for ULY_U8).
  *
  * Errors.  Every argument check of a call (and of every member of a
  *   grouped call) runs before anything is enqueued, so a rejected call
@@ -92,10 +93,11 @@ typedef enum {
     ULY_E_OVERLAP = -8       /* an input's memory range overlaps its destination's */
 } uly_status;
 
-/* 16-bit element types.  The relayout moves opaque bytes; the dtype only
- * matters to the fused norm + RoPE and to the target cache key ([UC
- * "element type"]). */
-typedef enum { ULY_F16 = 1, ULY_BF16 = 2 } uly_dtype;
+/* Element types.  The relayouts move opaque bytes, so ULY_U8 carries any
+ * 1-byte payload (fp8, int8) in the same byte budget; the dtype matters to
+ * the fused norm + RoPE (16-bit floats only) and to the target cache key
+ * ([UC "element type"]). */
+typedef enum { ULY_F16 = 1, ULY_BF16 = 2, ULY_U8 = 3 } uly_dtype;
 
 /* Direction of a target, part of its cache key. */
 typedef enum {
@@ -193,6 +195,19 @@ uly_status fused_qk_norm_rope_scatter(uly_ctx *ctx, const uly_tensor *q, const u
                                       int64_t table_rows, const char *const tags[3],
                                       void *const outs[3], hipStream_t caller);
 
+/* The same fused scatter into the packed receive layout ([QN "Description", Layouts:
+ * the "fused" payload): one target [P][B][S][Hl][3D] whose head rows hold
+ * q, k and v side by side,
+ *     Y[q'][b][g][j][c*D + d] = (normalised and rotated q, k, or v)[...][d]
+ * for c = 0 (q), 1 (k), 2 (v).  q, k and v are all required and share H.
+ * tag: cache key of the packed target (shape [B, P*S_l, H/P, 3*D]), or NULL
+ * with an explicit `out`. */
+uly_status fused_qkv_norm_rope_scatter_packed(uly_ctx *ctx, const uly_tensor *q, const uly_tensor *k,
+                                              const uly_tensor *v, const void *w_q, const void *w_k,
+                                              float eps, const float *cos_tab, const float *sin_tab,
+                                              int64_t table_rows, const char *tag, void *out,
+                                              hipStream_t caller);
+
 /* Grouped completion handshake ([P27 "Changes Made": one grouped handshake
  * for the tagged Q/K/V transfers]): make `consumer` wait, without any
  * host or device-wide synchronisation, for every scatter submitted since
@@ -207,6 +222,15 @@ uly_status uly_wait(uly_ctx *ctx, hipStream_t consumer);
  *     with an explicit `out`.  Runs on `caller`. */
 uly_status ulysses_gather_out(uly_ctx *ctx, const uly_tensor *o, const char *tag, void *out,
                               hipStream_t caller);
+
+/* Destination-major chunk exchange ([UC "Transforms": exchange_chunks]):
+ * each rank's payload is already packed destination-major as x[r][q][:]
+ * (chunk_bytes bytes per destination); the exchange delivers
+ *     y[q][r][:] = x[r][q][:]
+ * and interleaves nothing.  x and y hold P*P*chunk_bytes bytes each, are
+ * 16-byte aligned and do not overlap; chunk_bytes % 16 == 0.  Opaque bytes,
+ * any element type.  Runs on `stream`. */
+uly_status uly_exchange_chunks(uly_ctx *ctx, const void *x, void *y, int64_t chunk_bytes, hipStream_t stream);
 
 /* ---- sequence padding (parallel_shard.py's role in [CA]'s ownership table) */
 

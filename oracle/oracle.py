@@ -53,6 +53,8 @@ def _load():
         lib.oracle_scatter.restype = ctypes.c_int
         lib.oracle_gather.argtypes = [vp, vp, sz, i64, i64, i64, i64, i64]
         lib.oracle_gather.restype = ctypes.c_int
+        lib.oracle_exchange_chunks.argtypes = [vp, vp, i64, i64]
+        lib.oracle_exchange_chunks.restype = None
         lib.oracle_norm_rope_rows.argtypes = [vp, vp, i64, i64, vp, ctypes.c_double, vp, vp, i64, vp]
         lib.oracle_norm_rope_rows.restype = ctypes.c_int
         lib.oracle_rope_table_1d.argtypes = [vp, vp, i64, i64, i64, ctypes.c_double]
@@ -121,6 +123,22 @@ def gather(o: np.ndarray) -> np.ndarray:
     rc = _load().oracle_gather(_p(o), _p(z), o.itemsize, P, B, S, Hl, D)
     assert rc == 0
     return z
+
+
+def exchange_chunks(x: np.ndarray) -> np.ndarray:
+    """x[P, P, ...] destination-major payloads -> y[P, P, ...], y[q, r] = x[r, q] (opaque bytes)."""
+    x = np.ascontiguousarray(x)
+    P = x.shape[0]
+    assert x.shape[1] == P
+    y = np.empty_like(x)
+    chunk = x.nbytes // (P * P) if P else 0
+    _load().oracle_exchange_chunks(_p(x), _p(y), P, chunk)
+    return y
+
+
+def pack_qkv(yq: np.ndarray, yk: np.ndarray, yv: np.ndarray) -> np.ndarray:
+    """The packed receive layout: head rows hold q, k and v side by side ([..., 3*D])."""
+    return np.concatenate([yq, yk, yv], axis=-1)
 
 
 # --------------------------------------------------------------------------

@@ -19,6 +19,8 @@
  *        halos, zero-filled missing halos at the image edge), and the
  *        ownership table row for parallel_shard.py (sequence padding,
  *        slicing, gathering and restoration).
+ *  [UC]  flashinfer UlyssesCommunicator(backend="pcie") PR, "What"
+ *        (Transforms: exchange_chunks over a destination-major payload).
  *  [QN]  flashinfer PR #6332 (QkvNormRopeExchangeOverlap), "Description"
  *        (each rank receives its head band of all tokens) and
  *        "Assumptions" (fp32 RMSNorm, eps 1e-6, one [head_dim] weight per
@@ -89,6 +91,20 @@ int oracle_gather(const void *o_, void *z_, size_t es, int64_t P, int64_t B,
                             memcpy(z + dst * es, o + src * es, es);
                         }
     return 0;
+}
+
+/* Destination-major chunk exchange [UC "What: Transforms", exchange_chunks]:
+ * rank r's payload is already packed destination-major, x[r][q][chunk];
+ * rank q receives rank r's chunk for it at y[q][r]:
+ *     y[q][r][:] = x[r][q][:]
+ * Nothing inside a chunk is interleaved. */
+void oracle_exchange_chunks(const void *x_, void *y_, int64_t P, int64_t chunk_bytes)
+{
+    const unsigned char *x = (const unsigned char *)x_;
+    unsigned char *y = (unsigned char *)y_;
+    for (int64_t r = 0; r < P; ++r)
+        for (int64_t q = 0; q < P; ++q)
+            memcpy(y + (q * P + r) * chunk_bytes, x + (r * P + q) * chunk_bytes, (size_t)chunk_bytes);
 }
 
 /* ------------------------------------------------------------------------

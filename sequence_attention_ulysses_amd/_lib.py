@@ -29,6 +29,7 @@ E_OVERLAP = -8
 
 F16 = 1
 BF16 = 2
+U8 = 3
 MODE_SCATTER = 0
 MODE_GATHER = 1
 ROUTE_KERNEL = 0
@@ -41,7 +42,8 @@ KERNEL_KINDS = {"scatter": K_SCATTER, "norm_rope": K_NORM_ROPE, "gather": K_GATH
 # Every symbol include/uly.h declares.
 EXPORTS = (
     "uly_create", "uly_destroy", "uly_target_register", "uly_target_lookup", "uly_target_count",
-    "ulysses_scatter_qkv", "fused_qk_norm_rope_scatter", "uly_wait", "ulysses_gather_out",
+    "ulysses_scatter_qkv", "fused_qk_norm_rope_scatter", "fused_qkv_norm_rope_scatter_packed", "uly_wait",
+    "ulysses_gather_out", "uly_exchange_chunks",
     "uly_seq_pad_shard", "uly_seq_unshard_trim", "uly_spatial_split_halo",
     "uly_spatial_gather_stacked", "uly_spatial_trim_concat", "uly_rope_table_1d",
     "uly_rope_table_3d", "uly_profile_enable", "uly_profile_read", "uly_profile_reset",
@@ -136,6 +138,8 @@ def load() -> ctypes.CDLL:
         "uly_target_count": [vp, ctypes.POINTER(i32)],
         "ulysses_scatter_qkv": [vp, P_T, P_T, P_T, TAGS, OUTS, vp],
         "fused_qk_norm_rope_scatter": [vp, P_T, P_T, P_T, vp, vp, f32, vp, vp, i64, TAGS, OUTS, vp],
+        "fused_qkv_norm_rope_scatter_packed": [vp, P_T, P_T, P_T, vp, vp, f32, vp, vp, i64, cp, vp, vp],
+        "uly_exchange_chunks": [vp, vp, vp, i64, vp],
         "uly_wait": [vp, vp],
         "ulysses_gather_out": [vp, P_T, cp, vp, vp],
         "uly_seq_pad_shard": [vp, vp, i32, i64, i64, i64, i64, vp, vp],

@@ -21,14 +21,18 @@ from . import _lib
 from ._lib import check
 
 _DTYPES = {torch.float16: _lib.F16, torch.bfloat16: _lib.BF16}
-_TORCH_DTYPES = {v: k for k, v in _DTYPES.items()}
+# 1-byte payloads (fp8, int8) move as opaque bytes
+for _name in ("uint8", "int8", "float8_e4m3fn", "float8_e5m2", "float8_e4m3fnuz", "float8_e5m2fnuz"):
+    if hasattr(torch, _name):
+        _DTYPES[getattr(torch, _name)] = _lib.U8
 
 
-def _dtype_code(t: torch.Tensor) -> int:
+def _dtype_code(t) -> int:
+    dtype = t.dtype if isinstance(t, torch.Tensor) else t
     try:
-        return _DTYPES[t.dtype]
+        return _DTYPES[dtype]
     except KeyError:
-        raise TypeError("only float16 and bfloat16 tensors are supported, got %s" % t.dtype) from None
+        raise TypeError("supported: float16, bfloat16 and 1-byte types; got %s" % dtype) from None
 
 
 def _stream_handle(stream) -> ctypes.c_void_p:
@@ -146,14 +150,15 @@ class UlyssesContext:
         is full the returned tensor is a one-shot buffer (not cached).
         """
         shape = tuple(int(s) for s in shape)
-        key = (tag, mode, dtype, shape)
+        code = _dtype_code(dtype)
+        key = (tag, mode, code, shape)           # the library's key: 1-byte types share one code
         t = self._targets.get(key)
         if t is not None:
-            return t
+            return t if t.dtype == dtype else t.view(dtype)
         numel = self.world_size * math.prod(shape)
         buf = torch.empty(numel, dtype=dtype, device=torch.device("cuda", self.device))
-        st = self._lib.uly_target_register(self._h(), tag.encode(), mode, _DTYPES[dtype],
-                                           _lib.int64_array(shape), buf.data_ptr(), numel * 2)
+        st = self._lib.uly_target_register(self._h(), tag.encode(), mode, code,
+                                           _lib.int64_array(shape), buf.data_ptr(), buf.numel() * buf.element_size())
         view = buf.view((self.world_size,) + shape)
         if st == _lib.E_CACHE_FULL:
             warnings.warn("Ulysses target cache is full; '%s' uses a one-shot buffer" % tag, RuntimeWarning,
@@ -169,7 +174,7 @@ class UlyssesContext:
             self._check_out(out, like.dtype, self.world_size * math.prod(shape), tag or "out")
             return out, True
         t = self.target(tag, mode, like.dtype, shape)
-        return t, (tag, mode, like.dtype, tuple(shape)) not in self._targets
+        return t, (tag, mode, _dtype_code(like.dtype), tuple(int(x) for x in shape)) not in self._targets
 
     # -- the exchange -----------------------------------------------------------
     def scatter_qkv(self, q=None, k=None, v=None, tags=("q", "k", "v"), out=None, stream=None):
@@ -245,6 +250,53 @@ class UlyssesContext:
               "fused_qk_norm_rope_scatter")
         return dests
 
+    def fused_qkv_norm_rope_scatter_packed(self, q, k, v, w_q, w_k, cos, sin, eps: float = 1e-6, tag="qkv",
+                                           out=None, stream=None):
+        """Q/K norm + RoPE scatter with V into one packed target [P, B, P*S_l, H/P, 3*D]:
+        each head row holds q, k and v side by side."""
+        P = self.world_size
+        self._on_device(q, k, v, w_q, w_k, cos, sin, out)
+        for x in (q, k, v):
+            if x.dim() != 5:
+                raise ValueError("operands must be 5-D [P, B, S_l, H, D]")
+        shape = (q.shape[1], q.shape[2] * P, q.shape[3] // P, 3 * q.shape[4])
+        if out is None and q.shape[3] % P == 0:
+            dest = self.target(tag, _lib.MODE_SCATTER, q.dtype, shape)
+            explicit = (tag, _lib.MODE_SCATTER, _dtype_code(q.dtype), shape) not in self._targets
+        else:
+            dest, explicit = out, out is not None
+            if out is not None:
+                self._check_out(out, q.dtype, P * math.prod(shape), tag or "out")
+        for w in (w_q, w_k):
+            if w.dtype != q.dtype or not w.is_contiguous() or w.numel() != q.shape[-1]:
+                raise ValueError("norm weights must be contiguous [D] tensors in the operand dtype")
+        for t in (cos, sin):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2 or t.shape[1] * 2 != q.shape[-1]:
+                raise ValueError("cos/sin tables must be contiguous fp32 [rows, D/2]")
+        check(self._lib.fused_qkv_norm_rope_scatter_packed(
+            self._h(), ctypes.byref(describe(q)), ctypes.byref(describe(k)), ctypes.byref(describe(v)),
+            w_q.data_ptr(), w_k.data_ptr(), float(eps), cos.data_ptr(), sin.data_ptr(), cos.shape[0],
+            tag.encode() if tag else None, dest.data_ptr() if explicit and dest is not None else None,
+            _stream_handle(stream)), "fused_qkv_norm_rope_scatter_packed")
+        return dest
+
+    def exchange_chunks(self, x, out=None, stream=None):
+        """Destination-major chunk exchange: x [P, P, ...] (rank r's chunk for q at x[r, q])
+        -> y [P, P, ...] with y[q, r] = x[r, q]; opaque bytes."""
+        P = self.world_size
+        self._on_device(x, out)
+        if x.dim() < 2 or x.shape[0] != P or x.shape[1] != P or not x.is_contiguous():
+            raise ValueError("x must be a contiguous [P, P, ...] tensor")
+        if out is None:
+            out = torch.empty_like(x)
+        elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+            raise ValueError("out must match x")
+        chunk = x.numel() * x.element_size() // (P * P)
+        check(self._lib.uly_exchange_chunks(self._h(), x.data_ptr() if x.numel() else None,
+                                            out.data_ptr() if out.numel() else None, chunk,
+                                            _stream_handle(stream)), "uly_exchange_chunks")
+        return out
+
     def wait(self, stream=None) -> None:
         """Grouped handshake: ``stream`` (default: current) waits for all scatters since the last wait."""
         check(self._lib.uly_wait(self._h(), _stream_handle(stream)), "uly_wait")
@@ -260,7 +312,7 @@ class UlyssesContext:
         shape = (o.shape[1], o.shape[2] // P, o.shape[3] * P, o.shape[4])
         if out is None and o.shape[2] % P == 0:
             dest = self.target(tag, _lib.MODE_GATHER, o.dtype, shape)
-            explicit = (tag, _lib.MODE_GATHER, o.dtype, shape) not in self._targets
+            explicit = (tag, _lib.MODE_GATHER, _dtype_code(o.dtype), tuple(int(x) for x in shape)) not in self._targets
         else:
             dest, explicit = out, out is not None
         check(self._lib.ulysses_gather_out(self._h(), ctypes.byref(describe(o)), tag.encode() if tag else None,

@@ -50,7 +50,7 @@ struct NormRopeOperand {
     uint16_t *dst;
     const uint16_t *w;
     int64_t s_rank, s_b, s_s, s_h;   // source element strides
-    int64_t d_q, d_b, d_g;           // destination element strides (rank, batch, global token)
+    int64_t d_q, d_b, d_g, d_j;      // destination element strides (rank, batch, global token, head)
     FastDiv hl;                      // heads per rank
     uint32_t H;
     uint32_t pad;

@@ -230,7 +230,7 @@ __device__ __forceinline__ Slot<DT> make_slot(const NormRopeArgs &a, uint32_t hh
     sl.d_g = sel3(oi, o0.d_g, o1.d_g, o2.d_g);
     sl.src = sel3(oi, o0.src, o1.src, o2.src) + int64_t(h) * sel3(oi, o0.s_h, o1.s_h, o2.s_h) + lane * 8;
     sl.dst = sel3(oi, o0.dst, o1.dst, o2.dst) + int64_t(qd) * sel3(oi, o0.d_q, o1.d_q, o2.d_q) +
-             int64_t(j) * a.D + lane * 8;
+             int64_t(j) * sel3(oi, o0.d_j, o1.d_j, o2.d_j) + lane * 8;
     sl.rope = oi < 2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) sl.w[i] = 0.f;

@@ -68,6 +68,10 @@ struct ProfRecord {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// 16-bit floats, or opaque single bytes (fp8 / int8 payloads, [UC "element type"]).
+bool valid_dtype(int dtype) { return dtype == ULY_F16 || dtype == ULY_BF16 || dtype == ULY_U8; }
+int64_t elem_size(int dtype) { return dtype == ULY_U8 ? 1 : 2; }
+
 struct Range {
     uintptr_t lo = 0, hi = 0;   // [lo, hi), empty when lo == hi
     bool overlaps(const Range &o) const { return lo < hi && o.lo < o.hi && lo < o.hi && o.lo < hi; }
@@ -80,14 +84,14 @@ struct Operand {
     int64_t rank_stride = 0;
     int64_t B = 0, S = 0, H = 0, D = 0;
     int64_t sb = 0, ss = 0, sh = 0;   // element strides
+    int64_t es = 2;                   // bytes per element
     Range range;
     bool empty() const { return B == 0 || S == 0; }
 };
 
 uly_status check_operand(const uly_tensor *t, const char *name, int P, Operand &o) {
     if (!t) return fail(ULY_E_INVAL, "%s: null descriptor", name);
-    if (t->dtype != ULY_F16 && t->dtype != ULY_BF16)
-        return fail(ULY_E_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+    if (!valid_dtype(t->dtype)) return fail(ULY_E_DTYPE, "%s: unknown dtype %d", name, t->dtype);
     if (t->reserved != 0) return fail(ULY_E_INVAL, "%s: reserved field must be 0", name);
     for (int i = 0; i < 4; ++i)
         if (t->shape[i] < 0) return fail(ULY_E_INVAL, "%s: negative extent in dim %d", name, i);
@@ -96,17 +100,19 @@ uly_status check_operand(const uly_tensor *t, const char *name, int P, Operand &
     if (t->stride[3] != 1) return fail(ULY_E_INVAL, "%s: head-dim stride must be 1", name);
     if (t->rank_stride < 0 || t->stride[0] < 0 || t->stride[1] < 0 || t->stride[2] < 0)
         return fail(ULY_E_INVAL, "%s: negative stride", name);
-    if ((t->shape[3] * 2) % 16 != 0)
-        return fail(ULY_E_INVAL, "%s: D * 2 bytes (%lld) is not a multiple of 16", name,
-                    (long long)(t->shape[3] * 2));
+    const int64_t es = elem_size(t->dtype);
+    if ((t->shape[3] * es) % 16 != 0)
+        return fail(ULY_E_INVAL, "%s: a head row of %lld bytes is not a multiple of 16", name,
+                    (long long)(t->shape[3] * es));
     const int64_t ext[4] = {P, t->shape[0], t->shape[1], t->shape[2]};
     const int64_t str[4] = {t->rank_stride, t->stride[0], t->stride[1], t->stride[2]};
     for (int i = 0; i < 4; ++i)
-        if (ext[i] > 1 && (str[i] * 2) % 16 != 0)
+        if (ext[i] > 1 && (str[i] * es) % 16 != 0)
             return fail(ULY_E_INVAL, "%s: byte stride of dim %d (%lld) is not a multiple of 16", name,
-                        i, (long long)(str[i] * 2));
+                        i, (long long)(str[i] * es));
     o.data = static_cast<const uint8_t *>(t->data);
     o.dtype = t->dtype;
+    o.es = es;
     o.rank_stride = t->rank_stride;
     o.B = t->shape[0];
     o.S = t->shape[1];
@@ -121,15 +127,15 @@ uly_status check_operand(const uly_tensor *t, const char *name, int P, Operand &
         int64_t maxoff = o.D - 1;
         for (int i = 0; i < 4; ++i) maxoff += (ext[i] - 1) * str[i];
         o.range.lo = reinterpret_cast<uintptr_t>(o.data);
-        o.range.hi = o.range.lo + uintptr_t(maxoff + 1) * 2u;
+        o.range.hi = o.range.lo + uintptr_t(maxoff + 1) * uintptr_t(es);
     }
     return ULY_OK;
 }
 
-Range dense_range(const void *p, int64_t elems) {
+Range byte_range(const void *p, int64_t bytes) {
     Range r;
     r.lo = reinterpret_cast<uintptr_t>(p);
-    r.hi = r.lo + uintptr_t(elems) * 2u;
+    r.hi = r.lo + uintptr_t(bytes);
     return r;
 }
 
@@ -327,15 +333,15 @@ void fill_plan(CopyPlan &p, const uint8_t *src, uint8_t *dst, const int64_t n[4]
 // head band q: Hl*D elements.
 uly_status plan_scatter(const Operand &x, int P, uint8_t *dst, CopyPlan &p) {
     const int64_t Hl = x.H / P, S = int64_t(P) * x.S;
-    const int64_t C = Hl * x.D * 2;    // chunk bytes
+    const int64_t C = Hl * x.D * x.es;   // chunk bytes
     const int64_t total = int64_t(P) * x.B * P * x.S * (C / 16);
     if (total >= kMaxVecs || x.S >= kMaxVecs || x.B >= kMaxVecs)
         return fail(ULY_E_UNSUPPORTED, "operand too large for one launch (%lld vectors)", (long long)total);
     // per-dim (source, destination) byte strides
-    const int64_t q_s = Hl * x.sh * 2, q_d = x.B * S * C;
-    const int64_t b_s = x.sb * 2, b_d = S * C;
-    const int64_t r_s = x.rank_stride * 2, r_d = x.S * C;
-    const int64_t s_s = x.ss * 2, s_d = C;
+    const int64_t q_s = Hl * x.sh * x.es, q_d = x.B * S * C;
+    const int64_t b_s = x.sb * x.es, b_d = S * C;
+    const int64_t r_s = x.rank_stride * x.es, r_d = x.S * C;
+    const int64_t s_s = x.ss * x.es, s_d = C;
     if (ULY_SCATTER_ORDER == 0) {     // destination order (q, b, r, s)
         const int64_t n[4] = {P, x.B, P, x.S}, ss[4] = {q_s, b_s, r_s, s_s}, ds[4] = {q_d, b_d, r_d, s_d};
         fill_plan(p, x.data, dst, n, ss, ds, C / 16, total);
@@ -350,14 +356,14 @@ uly_status plan_scatter(const Operand &x, int P, uint8_t *dst, CopyPlan &p) {
 // [P(r)][B][S_l][P(q)*Hl][D].
 uly_status plan_gather(const Operand &o, int P, uint8_t *dst, CopyPlan &p) {
     const int64_t S_l = o.S / P, H = o.H * P;
-    const int64_t C = o.H * o.D * 2;
+    const int64_t C = o.H * o.D * o.es;
     const int64_t total = int64_t(P) * o.B * S_l * P * (C / 16);
     if (total >= kMaxVecs || o.S >= kMaxVecs || o.B >= kMaxVecs)
         return fail(ULY_E_UNSUPPORTED, "operand too large for one launch (%lld vectors)", (long long)total);
-    const int64_t r_s = S_l * o.ss * 2, r_d = o.B * S_l * H * o.D * 2;
-    const int64_t b_s = o.sb * 2, b_d = S_l * H * o.D * 2;
-    const int64_t s_s = o.ss * 2, s_d = H * o.D * 2;
-    const int64_t q_s = o.rank_stride * 2, q_d = C;
+    const int64_t r_s = S_l * o.ss * o.es, r_d = o.B * S_l * H * o.D * o.es;
+    const int64_t b_s = o.sb * o.es, b_d = S_l * H * o.D * o.es;
+    const int64_t s_s = o.ss * o.es, s_d = H * o.D * o.es;
+    const int64_t q_s = o.rank_stride * o.es, q_d = C;
     if (ULY_GATHER_ORDER == 0) {      // destination order (r, b, s, q)
         const int64_t n[4] = {P, o.B, S_l, P}, ss[4] = {r_s, b_s, s_s, q_s}, ds[4] = {r_d, b_d, s_d, q_d};
         fill_plan(p, o.data, dst, n, ss, ds, C / 16, total);
@@ -372,13 +378,13 @@ uly_status plan_gather(const Operand &o, int P, uint8_t *dst, CopyPlan &p) {
 // Hl*D elements at the source token pitch, landing as one dense run in the
 // destination [P(q)][B][S][Hl][D].
 hipError_t copy_engine_scatter(const Operand &x, int P, uint8_t *dst, hipStream_t s) {
-    const int64_t Hl = x.H / P, S = int64_t(P) * x.S, C = Hl * x.D * 2;
+    const int64_t Hl = x.H / P, S = int64_t(P) * x.S, C = Hl * x.D * x.es;
     for (int64_t r = 0; r < P; ++r)
         for (int64_t q = 0; q < P; ++q)
             for (int64_t b = 0; b < x.B; ++b) {
-                const uint8_t *src = x.data + 2 * (r * x.rank_stride + b * x.sb + q * Hl * x.sh);
+                const uint8_t *src = x.data + x.es * (r * x.rank_stride + b * x.sb + q * Hl * x.sh);
                 uint8_t *d = dst + ((q * x.B + b) * S + r * x.S) * C;
-                const size_t pitch = x.S > 1 ? size_t(x.ss * 2) : size_t(C);
+                const size_t pitch = x.S > 1 ? size_t(x.ss * x.es) : size_t(C);
                 hipError_t e = hipMemcpy2DAsync(d, size_t(C), src, pitch, size_t(C), size_t(x.S),
                                                 hipMemcpyDeviceToDeviceNoCU, s);
                 if (e != hipSuccess) return e;
@@ -496,7 +502,7 @@ uly_status uly_target_register(uly_ctx *c, const char *tag, int mode, int dtype,
     if (st != ULY_OK) return st;
     if (!valid_tag(tag)) return fail(ULY_E_INVAL, "tag must be 1..%d bytes", kTagMax);
     if (mode != ULY_MODE_SCATTER && mode != ULY_MODE_GATHER) return fail(ULY_E_INVAL, "bad mode %d", mode);
-    if (dtype != ULY_F16 && dtype != ULY_BF16) return fail(ULY_E_DTYPE, "bad dtype %d", dtype);
+    if (!valid_dtype(dtype)) return fail(ULY_E_DTYPE, "bad dtype %d", dtype);
     if (!shape) return fail(ULY_E_INVAL, "null shape");
     int64_t elems = c->P;
     for (int i = 0; i < 4; ++i) {
@@ -504,9 +510,9 @@ uly_status uly_target_register(uly_ctx *c, const char *tag, int mode, int dtype,
         elems *= shape[i];
     }
     if (!storage || !aligned16(storage)) return fail(ULY_E_INVAL, "storage null or not 16-byte aligned");
-    if (bytes < size_t(elems) * 2u)
+    if (bytes < size_t(elems * elem_size(dtype)))
         return fail(ULY_E_INVAL, "storage of %zu bytes is smaller than the %lld bytes of P slabs", bytes,
-                    (long long)(elems * 2));
+                    (long long)(elems * elem_size(dtype)));
     if (find_target(c, tag, mode, dtype, shape))
         return fail(ULY_E_INVAL, "target '%s' with this key is already registered", tag);
     if (int(c->targets.size()) >= c->max_targets)
@@ -583,7 +589,7 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
             return st;
         dsts[i] = dst;
         in_ranges.push_back(x.range);
-        out_ranges.push_back(dense_range(dst, int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3]));
+        out_ranges.push_back(byte_range(dst, int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3] * x.es));
         if ((st = plan_scatter(x, c->P, dst, batch.p[batch.n])) != ULY_OK) return st;
         batch.n++;
     }
@@ -596,7 +602,7 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
     if (c->route == ULY_ROUTE_COPY_ENGINE)
         for (int i = 0; i < 3; ++i)
-            if (mem[i] && !ops[i].empty() && ops[i].S > 1 && ops[i].ss * 2 < (ops[i].H / c->P) * ops[i].D * 2)
+            if (mem[i] && !ops[i].empty() && ops[i].S > 1 && ops[i].ss < (ops[i].H / c->P) * ops[i].D)
                 return fail(ULY_E_UNSUPPORTED, "%s: copy engines need a token pitch of at least one head band",
                             names[i]);
     if ((st = fork_comm(c, caller)) != ULY_OK) return st;
@@ -619,10 +625,12 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
     return mark_pending(c, c->comm);
 }
 
-uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly_tensor *k, const uly_tensor *v,
-                                      const void *w_q, const void *w_k, float eps, const float *cos_tab,
-                                      const float *sin_tab, int64_t table_rows, const char *const tags[3],
-                                      void *const outs[3], hipStream_t caller) {
+// The fused Q/K norm + RoPE scatter, into three targets or (packed) into one
+// [P][B][S][Hl][3D] target whose head rows hold q, k and v side by side.
+static uly_status fused_scatter(uly_ctx *c, const uly_tensor *q, const uly_tensor *k, const uly_tensor *v,
+                                const void *w_q, const void *w_k, float eps, const float *cos_tab,
+                                const float *sin_tab, int64_t table_rows, const char *const tags[3],
+                                void *const outs[3], hipStream_t caller, bool packed) {
     uly_status st = ctx_ok(c);
     if (st != ULY_OK) return st;
     const uly_tensor *mem[3] = {q, k, v};
@@ -654,6 +662,9 @@ uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly
             return fail(ULY_E_INVAL, "%s: weight pointer null or not 16-byte aligned", names[i]);
     }
     if (present == 0) return fail(ULY_E_INVAL, "no operand given");
+    if (dtype == ULY_U8) return fail(ULY_E_UNSUPPORTED, "the fused norm + RoPE takes 16-bit operands");
+    if (packed && (!q || !k || !v || ops[0].H != ops[1].H || ops[0].H != ops[2].H))
+        return fail(ULY_E_INVAL, "the packed layout needs q, k and v with the same head count");
     const int lanes = int(D * 2 / 16);
     if (D % 2 != 0 || !(lanes == 4 || lanes == 8 || lanes == 16 || lanes == 32))
         return fail(ULY_E_UNSUPPORTED, "head dim %lld not supported (32, 64, 128 or 256)", (long long)D);
@@ -665,17 +676,21 @@ uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly
     for (int i = 0; i < 3; ++i) {
         if (!mem[i] || ops[i].empty()) continue;
         const Operand &x = ops[i];
-        const int64_t tshape[4] = {x.B, x.S * c->P, x.H / c->P, x.D};
-        if ((st = resolve_target(c, names[i], tags ? tags[i] : nullptr, outs ? outs[i] : nullptr,
-                                 ULY_MODE_SCATTER, x.dtype, tshape, dsts[i])) != ULY_OK)
-            return st;
         in_ranges.push_back(x.range);
-        out_ranges.push_back(dense_range(dsts[i], int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3]));
+        if (packed && i > 0) {
+            dsts[i] = dsts[0] + i * x.D * 2;     // the k and v columns of the one packed target
+            continue;
+        }
+        const int64_t tshape[4] = {x.B, x.S * c->P, x.H / c->P, packed ? 3 * x.D : x.D};
+        if ((st = resolve_target(c, packed ? "qkv" : names[i], tags ? tags[i] : nullptr,
+                                 outs ? outs[i] : nullptr, ULY_MODE_SCATTER, x.dtype, tshape, dsts[i])) != ULY_OK)
+            return st;
+        out_ranges.push_back(byte_range(dsts[i], int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3] * 2));
     }
-    in_ranges.push_back(dense_range(cos_tab, table_rows * D));   // fp32 [rows][D/2] = rows*D halves
-    in_ranges.push_back(dense_range(sin_tab, table_rows * D));
-    if (w_q) in_ranges.push_back(dense_range(w_q, D));
-    if (w_k) in_ranges.push_back(dense_range(w_k, D));
+    in_ranges.push_back(byte_range(cos_tab, table_rows * (D / 2) * 4));   // fp32 [rows][D/2]
+    in_ranges.push_back(byte_range(sin_tab, table_rows * (D / 2) * 4));
+    if (w_q) in_ranges.push_back(byte_range(w_q, D * 2));
+    if (w_k) in_ranges.push_back(byte_range(w_k, D * 2));
     if ((st = check_overlaps(in_ranges, out_ranges)) != ULY_OK) return st;
 
     NormRopeArgs a{};
@@ -694,9 +709,11 @@ uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly
         o.s_b = x.sb;
         o.s_s = x.ss;
         o.s_h = x.sh;
-        o.d_q = x.B * Sg * Hl * x.D;
-        o.d_b = Sg * Hl * x.D;
-        o.d_g = Hl * x.D;
+        const int64_t row = packed ? 3 * x.D : x.D;    // destination elements per head row
+        o.d_q = x.B * Sg * Hl * row;
+        o.d_b = Sg * Hl * row;
+        o.d_g = Hl * row;
+        o.d_j = row;
         o.hl = FastDiv::make(uint32_t(Hl));
         o.H = uint32_t(x.H);
         Hrows[i] = uint32_t(x.H);
@@ -732,6 +749,22 @@ uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly
                      [&] { launch_norm_rope(a, lanes, dtype, uniform, tile, blocks, caller); })) != ULY_OK)
         return st;
     return mark_pending(c, caller);
+}
+
+uly_status fused_qk_norm_rope_scatter(uly_ctx *c, const uly_tensor *q, const uly_tensor *k, const uly_tensor *v,
+                                      const void *w_q, const void *w_k, float eps, const float *cos_tab,
+                                      const float *sin_tab, int64_t table_rows, const char *const tags[3],
+                                      void *const outs[3], hipStream_t caller) {
+    return fused_scatter(c, q, k, v, w_q, w_k, eps, cos_tab, sin_tab, table_rows, tags, outs, caller, false);
+}
+
+uly_status fused_qkv_norm_rope_scatter_packed(uly_ctx *c, const uly_tensor *q, const uly_tensor *k,
+                                              const uly_tensor *v, const void *w_q, const void *w_k, float eps,
+                                              const float *cos_tab, const float *sin_tab, int64_t table_rows,
+                                              const char *tag, void *out, hipStream_t caller) {
+    const char *tags[3] = {tag, nullptr, nullptr};
+    void *outs[3] = {out, nullptr, nullptr};
+    return fused_scatter(c, q, k, v, w_q, w_k, eps, cos_tab, sin_tab, table_rows, tags, outs, caller, true);
 }
 
 uly_status uly_wait(uly_ctx *c, hipStream_t consumer) {
@@ -770,7 +803,7 @@ uly_status ulysses_gather_out(uly_ctx *c, const uly_tensor *o, const char *tag, 
         uint8_t *dst = nullptr;
         if ((st = resolve_target(c, "out", tag, out, ULY_MODE_GATHER, x.dtype, tshape, dst)) != ULY_OK) return st;
         std::vector<Range> in{x.range};
-        std::vector<Range> outs{dense_range(dst, int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3])};
+        std::vector<Range> outs{byte_range(dst, int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * tshape[3] * x.es)};
         if ((st = check_overlaps(in, outs)) != ULY_OK) return st;
         if ((st = plan_gather(x, c->P, dst, batch.p[0])) != ULY_OK) return st;
         batch.n = 1;
@@ -783,24 +816,52 @@ uly_status ulysses_gather_out(uly_ctx *c, const uly_tensor *o, const char *tag, 
     return launch(c, ULY_K_GATHER, caller, [&] { launch_relayout(batch, caller); });
 }
 
+uly_status uly_exchange_chunks(uly_ctx *c, const void *x, void *y, int64_t chunk_bytes, hipStream_t stream) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    if (chunk_bytes < 0 || chunk_bytes % 16 != 0)
+        return fail(ULY_E_INVAL, "chunk of %lld bytes is not a non-negative multiple of 16", (long long)chunk_bytes);
+    const int64_t P = c->P, total_bytes = P * P * chunk_bytes;
+    if (total_bytes / 16 >= kMaxVecs) return fail(ULY_E_UNSUPPORTED, "too large for one launch");
+    CopyBatch batch{};
+    if (total_bytes > 0) {
+        if (!x || !y || !aligned16(x) || !aligned16(y)) return fail(ULY_E_INVAL, "x, y null or not 16-byte aligned");
+        if (byte_range(x, total_bytes).overlaps(byte_range(y, total_bytes)))
+            return fail(ULY_E_OVERLAP, "x and y overlap");
+        // y[q][r][:] = x[r][q][:], iterated in destination order (q, r)
+        const int64_t n[4] = {P, P, 1, 1}, ss[4] = {chunk_bytes, P * chunk_bytes, 0, 0},
+                      ds[4] = {P * chunk_bytes, chunk_bytes, 0, 0};
+        fill_plan(batch.p[0], static_cast<const uint8_t *>(x), static_cast<uint8_t *>(y), n, ss, ds,
+                  chunk_bytes / 16, total_bytes / 16);
+        batch.n = 1;
+    }
+    if ((st = finish_batch(batch)) != ULY_OK) return st;
+    if (c->host_only) return host_only_launch(c);
+    if (batch.n == 0) return ULY_OK;
+    DeviceGuard g(c->device);
+    if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
+    return launch(c, ULY_K_SCATTER, stream, [&] { launch_relayout(batch, stream); });
+}
+
 // ---- sequence padding ------------------------------------------------------
 
 static uly_status rowmap_common(uly_ctx *c, const void *src, int dtype, int64_t row_elems, void *dst,
                                 int64_t src_rows, int64_t dst_rows, RowMapArgs &a) {
     uly_status st = ctx_ok(c);
     if (st != ULY_OK) return st;
-    if (dtype != ULY_F16 && dtype != ULY_BF16) return fail(ULY_E_DTYPE, "bad dtype %d", dtype);
-    if (row_elems < 1 || (row_elems * 2) % 16 != 0)
+    if (!valid_dtype(dtype)) return fail(ULY_E_DTYPE, "bad dtype %d", dtype);
+    const int64_t es = elem_size(dtype);
+    if (row_elems < 1 || (row_elems * es) % 16 != 0)
         return fail(ULY_E_INVAL, "row of %lld elements is not a positive multiple of 16 bytes",
                     (long long)row_elems);
     if (src_rows < 0 || dst_rows < 0) return fail(ULY_E_INVAL, "negative extent");
-    const int64_t vpr = row_elems * 2 / 16;
+    const int64_t vpr = row_elems * es / 16;
     const int64_t total = dst_rows * vpr;
     if (total >= kMaxVecs || src_rows * vpr >= kMaxVecs) return fail(ULY_E_UNSUPPORTED, "too large for one launch");
     if (total > 0) {
         if (!dst || !aligned16(dst)) return fail(ULY_E_INVAL, "destination null or not 16-byte aligned");
         if (src_rows > 0 && (!src || !aligned16(src))) return fail(ULY_E_INVAL, "source null or not 16-byte aligned");
-        if (dense_range(src, src_rows * row_elems).overlaps(dense_range(dst, dst_rows * row_elems)))
+        if (byte_range(src, src_rows * row_elems * es).overlaps(byte_range(dst, dst_rows * row_elems * es)))
             return fail(ULY_E_OVERLAP, "source and destination overlap");
     }
     a = RowMapArgs{};

@@ -39,8 +39,18 @@ def norm_weight(D: int, dtype: str, seed: int, device="cpu") -> torch.Tensor:
     return normal((D,), dtype, seed, device, mean=1.0, std=0.1)
 
 
+def random_bytes(shape, seed: int, dtype: torch.dtype = torch.uint8, device="cpu") -> torch.Tensor:
+    """Uniform random bytes viewed as a 1-byte dtype (fp8 / int8 payloads as opaque bits)."""
+    g = generator(seed, "cpu")
+    t = torch.randint(0, 256, tuple(shape), generator=g, dtype=torch.uint8)
+    return t.view(dtype).to(device)
+
+
 def bits(t: torch.Tensor):
-    """16-bit storage of a CPU tensor as a numpy uint16 array (bf16 has no numpy dtype)."""
+    """Storage of a CPU tensor as numpy unsigned words: uint16 for 16-bit types (bf16
+    has no numpy dtype), uint8 for 1-byte types."""
+    if t.element_size() == 1:
+        return t.contiguous().view(torch.uint8).numpy()
     return t.contiguous().view(torch.int16).numpy().view("uint16")
 
 

@@ -701,3 +701,82 @@ def test_copy_engine_route(dev, orc, P, B, S_l, Hq, Hkv, D, fused):
         torch.cuda.synchronize()
         for y, y2 in zip(ys, ys2):
             assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# 1-byte payloads, the packed receive layout, the destination-major exchange
+# ---------------------------------------------------------------------------
+BYTE_DTYPES = [torch.uint8, torch.int8, torch.float8_e4m3fn, torch.float8_e5m2]
+
+
+@pytest.mark.parametrize("P,B,S_l,Hq,Hkv,D", [(4, 1, 33, 8, 8, 128), (8, 2, 5, 16, 8, 16), (2, 1, 200, 4, 2, 64),
+                                              (4, 1, 4096, 24, 24, 128)])
+def test_byte_payloads_bit_exact(dev, orc, P, B, S_l, Hq, Hkv, D):
+    """flashinfer UlyssesCommunicator PR, 'What': fp8 / int8 move as opaque bytes,
+    byte-exact in both directions."""
+    for i, dt in enumerate(BYTE_DTYPES):
+        q = synth.random_bytes((P, B, S_l, Hq, D), 40 + i, dt, dev)
+        k = synth.random_bytes((P, B, S_l, Hkv, D), 50 + i, dt, dev)
+        v = synth.random_bytes((P, B, S_l, Hkv, D), 60 + i, dt, dev)
+        with UlyssesContext(P, device=0) as ctx:
+            ys = ctx.scatter_qkv(q, k, v)
+            ctx.wait()
+            torch.cuda.synchronize()
+            for x, y in zip((q, k, v), ys):
+                assert y.dtype == dt
+                np.testing.assert_array_equal(to_bits(y), orc.scatter(to_bits(x)))
+            o = synth.random_bytes((P, B, P * S_l, Hq // P, D), 70 + i, dt, dev)
+            z = ctx.gather_out(o)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(to_bits(z), orc.gather(to_bits(o)))
+
+
+@pytest.mark.parametrize("P,B,S_l,H,D,dtype,fused", [(4, 1, 200, 24, 128, "bf16", True), (2, 1, 128, 8, 64, "f16", False),
+                                                     (2, 2, 37, 6, 128, "bf16", False), (4, 1, 29, 8, 32, "bf16", True),
+                                                     (2, 1, 50, 4, 256, "f16", False)])
+def test_packed_receive_layout(dev, orc, P, B, S_l, H, D, dtype, fused):
+    """flashinfer PR #6332, 'Description' (Layouts): the fused [B, S, Hl, 3D] payload
+    holds q, k and v side by side in every head row."""
+    if fused:
+        qkv = synth.normal((P, B, S_l, 3, H, D), dtype, 31, dev)
+        q, k, v = qkv[:, :, :, 0], qkv[:, :, :, 1], qkv[:, :, :, 2]
+    else:
+        q, k, v = contiguous_qkv(P, B, S_l, H, D, dtype, 31, dev)
+    w_q = synth.norm_weight(D, dtype, 3, dev)
+    w_k = synth.norm_weight(D, dtype, 4, dev)
+    rows = P * S_l
+    cos, sin = rope_table_1d(rows, D)
+    ocos, osin = orc.rope_table_1d(rows, D)
+    with UlyssesContext(P, device=0) as ctx:
+        y = ctx.fused_qkv_norm_rope_scatter_packed(q, k, v, w_q, w_k, cos.to(dev), sin.to(dev))
+        assert tuple(y.shape) == (P, B, P * S_l, H // P, 3 * D)
+        yq, yk, yv = ctx.fused_qk_norm_rope_scatter(q, k, w_q, w_k, cos.to(dev), sin.to(dev), v=v)
+        ctx.wait()
+        torch.cuda.synchronize()
+        # the same arithmetic as the three-target layout, bit for bit
+        assert torch.equal(y.view(torch.int16), torch.cat([yq, yk, yv], dim=-1).view(torch.int16))
+        ref_q = orc.fused_norm_rope_scatter(to_bits(q), dtype, to_bits(w_q), 1e-6, ocos, osin)
+        ref_k = orc.fused_norm_rope_scatter(to_bits(k), dtype, to_bits(w_k), 1e-6, ocos, osin)
+        assert_close16(y[..., :D], ref_q, dtype, "q")
+        assert_close16(y[..., D:2 * D], ref_k, dtype, "k")
+        np.testing.assert_array_equal(to_bits(y[..., 2 * D:]), orc.scatter(to_bits(v)))
+        # a second call reuses the cached packed target
+        y2 = ctx.fused_qkv_norm_rope_scatter_packed(q, k, v, w_q, w_k, cos.to(dev), sin.to(dev))
+        torch.cuda.synchronize()
+        assert y2.data_ptr() == y.data_ptr()
+
+
+@pytest.mark.parametrize("P,chunk", [(1, 4096), (2, 16), (4, 1 << 20), (8, 48), (4, 0)])
+def test_exchange_chunks_bit_exact(dev, orc, P, chunk):
+    """flashinfer UlyssesCommunicator PR, 'What' (Transforms): y[q, r] = x[r, q]."""
+    x = synth.random_bytes((P, P, chunk), 80 + P, torch.uint8, dev)
+    with UlyssesContext(P, device=0) as ctx:
+        y = ctx.exchange_chunks(x)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), orc.exchange_chunks(x.cpu().numpy()))
+        # bf16 payload of a pack that laid rows out destination-major
+        if chunk and chunk % 2 == 0:
+            xb = synth.normal((P, P, chunk // 2), "bf16", 90, dev)
+            yb = ctx.exchange_chunks(xb)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(to_bits(yb), orc.exchange_chunks(to_bits(xb)))

@@ -356,3 +356,82 @@ def test_profile_arguments(lib, ctx4):
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.uly_profile_read(ctx4.h, 9, ctypes.byref(ms), ctypes.byref(n)) == _lib.E_INVAL
     assert lib.uly_profile_read(ctx4.h, 1, ctypes.byref(ms), ctypes.byref(n)) == _lib.OK and n.value == 0
+
+
+# ---------------------------------------------------------------------------
+# 1-byte payloads, the packed receive layout, the destination-major exchange
+# ---------------------------------------------------------------------------
+def test_byte_payloads_accepted_by_relayouts(lib, ctx4):
+    """flashinfer UlyssesCommunicator PR, 'What': fp8 / int8 ride as opaque bytes."""
+    shape, t_shape = (1, 16, 8, 128), (1, 64, 2, 128)
+    assert register(lib, ctx4, "q", _lib.MODE_SCATTER, t_shape, BASE + 64 * MiB, dtype=_lib.U8,
+                    nbytes=4 * 64 * 2 * 128) == _lib.OK
+    q = T(BASE, shape, dtype=_lib.U8)
+    assert scatter(lib, ctx4, q=q, tags=("q", None, None)) == _lib.E_UNSUPPORTED        # would launch
+    # a 16-element head row is 16 bytes: the smallest one-byte row
+    q16 = T(BASE, (1, 16, 8, 16), dtype=_lib.U8)
+    st = scatter(lib, ctx4, q=q16, tags=("q", None, None), outs=(BASE + 64 * MiB, None, None))
+    assert st == _lib.E_UNSUPPORTED
+    q8 = T(BASE, (1, 16, 8, 8), dtype=_lib.U8)
+    st = scatter(lib, ctx4, q=q8, tags=("q", None, None), outs=(BASE + 64 * MiB, None, None))
+    assert st == _lib.E_INVAL and b"multiple of 16" in lib.uly_last_error()
+    # storage is sized in bytes: the two-byte requirement would be twice as large
+    assert register(lib, ctx4, "k", _lib.MODE_SCATTER, t_shape, BASE + 80 * MiB, dtype=_lib.U8,
+                    nbytes=4 * 64 * 2 * 128 - 16) == _lib.E_INVAL
+    # the overlap check counts bytes too: a destination one byte-slab past the source is fine
+    src = T(BASE, shape, dtype=_lib.U8)
+    st = scatter(lib, ctx4, q=src, tags=("q", None, None), outs=(BASE + 16 * 8 * 128, None, None))
+    assert st == _lib.E_OVERLAP                  # source covers 4 ranks x 16 x 8 x 128 bytes
+    st = scatter(lib, ctx4, q=src, tags=("q", None, None), outs=(BASE + 4 * 16 * 8 * 128, None, None))
+    assert st == _lib.E_UNSUPPORTED
+    o = T(BASE, (1, 64, 2, 128), dtype=_lib.U8)
+    assert lib.ulysses_gather_out(ctx4.h, ctypes.byref(o), None, BASE + 64 * MiB, None) == _lib.E_UNSUPPORTED
+    assert lib.uly_seq_pad_shard(ctx4.h, BASE, _lib.U8, 1, 100, 16, 25, BASE + 64 * MiB, None) == _lib.E_UNSUPPORTED
+    assert lib.uly_seq_pad_shard(ctx4.h, BASE, _lib.U8, 1, 100, 8, 25, BASE + 64 * MiB, None) == _lib.E_INVAL
+
+
+def test_fused_refuses_byte_payloads(lib, ctx4):
+    q, k = T(BASE, (1, 16, 8, 128), dtype=_lib.U8), T(BASE + 64 * MiB, (1, 16, 8, 128), dtype=_lib.U8)
+    assert _fused(lib, ctx4, q, k) == _lib.E_UNSUPPORTED and b"16-bit" in lib.uly_last_error()
+
+
+def _packed(lib, c, q, k, v, out=BASE + 100 * MiB, tag=None, rows=64, eps=1e-6):
+    args = [ctypes.byref(x) if x is not None else None for x in (q, k, v)]
+    return lib.fused_qkv_norm_rope_scatter_packed(c.h, *args, BASE + 200 * MiB, BASE + 201 * MiB, eps,
+                                                  BASE + 300 * MiB, BASE + 310 * MiB, rows,
+                                                  tag.encode() if tag else None, out, None)
+
+
+def test_packed_layout_checks(lib, ctx4):
+    shape = (1, 16, 8, 128)
+    q, k, v = T(BASE, shape), T(BASE + 64 * MiB, shape), T(BASE + 80 * MiB, shape)
+    assert _packed(lib, ctx4, q, k, v) == _lib.E_UNSUPPORTED and b"host-only" in lib.uly_last_error()
+    assert _packed(lib, ctx4, q, k, None) == _lib.E_INVAL                      # all three required
+    assert _packed(lib, ctx4, None, k, v) == _lib.E_INVAL
+    k4 = T(BASE + 64 * MiB, (1, 16, 4, 128))
+    assert _packed(lib, ctx4, q, k4, v) == _lib.E_INVAL and b"same head count" in lib.uly_last_error()
+    # the one packed target spans P * B * S * Hl * 3D elements: 4*64*2*384*2 bytes
+    span = 4 * 64 * 2 * 384 * 2
+    v_in_target = T(BASE + 100 * MiB + span - 4096, shape)
+    assert _packed(lib, ctx4, q, k, v_in_target) == _lib.E_OVERLAP
+    v_after = T(BASE + 100 * MiB + span, shape)
+    assert _packed(lib, ctx4, q, k, v_after) == _lib.E_UNSUPPORTED
+    # a tagged packed target is keyed by its [B, S, Hl, 3D] shape
+    assert _packed(lib, ctx4, q, k, v, out=None, tag="qkv") == _lib.E_NOT_FOUND
+    assert register(lib, ctx4, "qkv", _lib.MODE_SCATTER, (1, 64, 2, 128), BASE + 100 * MiB) == _lib.OK
+    assert _packed(lib, ctx4, q, k, v, out=None, tag="qkv") == _lib.E_NOT_FOUND
+    assert register(lib, ctx4, "qkv", _lib.MODE_SCATTER, (1, 64, 2, 384), BASE + 120 * MiB,
+                    nbytes=span) == _lib.OK
+    assert _packed(lib, ctx4, q, k, v, out=None, tag="qkv") == _lib.E_UNSUPPORTED
+
+
+def test_exchange_chunks_checks(lib, ctx4):
+    """flashinfer UlyssesCommunicator PR, 'What' (Transforms): a destination-major exchange."""
+    ex = lib.uly_exchange_chunks
+    assert ex(ctx4.h, BASE, BASE + 64 * MiB, 4096, None) == _lib.E_UNSUPPORTED       # would launch
+    assert ex(ctx4.h, BASE, BASE + 64 * MiB, 24, None) == _lib.E_INVAL               # not 16-byte chunks
+    assert ex(ctx4.h, BASE, BASE + 64 * MiB, -16, None) == _lib.E_INVAL
+    assert ex(ctx4.h, BASE + 8, BASE + 64 * MiB, 16, None) == _lib.E_INVAL          # misaligned
+    assert ex(ctx4.h, None, BASE, 16, None) == _lib.E_INVAL
+    assert ex(ctx4.h, BASE, BASE + 16 * 4096 - 16, 4096, None) == _lib.E_OVERLAP   # 16 chunks of 4 KiB
+    assert ex(ctx4.h, BASE, BASE + 16 * 4096, 4096, None) == _lib.E_UNSUPPORTED

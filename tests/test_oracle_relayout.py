@@ -190,3 +190,37 @@ def test_spatial_round_trip_and_halos(orc, shape, P):
     for r in range(P):
         assert (st[r][..., h[r]:, :] == 0).all()
     np.testing.assert_array_equal(orc.spatial_trim_concat(st, Hh), full)
+
+
+# ---------------------------------------------------------------------------
+# destination-major chunk exchange
+# ---------------------------------------------------------------------------
+def test_exchange_chunks_golden(orc):
+    g = json.load(open(os.path.join(GOLDEN, "exchange_chunks_p3_labels.json")))
+    table = {}
+    x = np.array(_labels_to_codes(g["input"], table), dtype=np.uint16)
+    want = np.array(_labels_to_codes(g["output"], table), dtype=np.uint16)
+    np.testing.assert_array_equal(orc.exchange_chunks(x), want)
+
+
+@pytest.mark.parametrize("P,chunk", [(1, 16), (2, 48), (4, 1536), (8, 16)])
+def test_exchange_chunks_transpose_and_involution(orc, P, chunk):
+    rng = np.random.default_rng(P * chunk)
+    x = rng.integers(0, 256, size=(P, P, chunk), dtype=np.uint8)
+    y = orc.exchange_chunks(x)
+    np.testing.assert_array_equal(y, x.transpose(1, 0, 2))          # library special case
+    np.testing.assert_array_equal(orc.exchange_chunks(y), x)         # applied twice: identity
+
+
+def test_byte_payload_scatter(orc):
+    """1-byte payloads (fp8 / int8) move as opaque bytes through the same map."""
+    rng = np.random.default_rng(9)
+    x = rng.integers(0, 256, size=(4, 2, 5, 8, 16), dtype=np.uint8)
+    np.testing.assert_array_equal(orc.scatter(x), _torch_scatter_bytes(x))
+    np.testing.assert_array_equal(orc.gather(orc.scatter(x)), x)
+
+
+def _torch_scatter_bytes(x):
+    P, B, S_l, H, D = x.shape
+    t = torch.from_numpy(x).view(P, B, S_l, P, H // P, D).permute(3, 1, 0, 2, 4, 5)
+    return t.reshape(P, B, P * S_l, H // P, D).contiguous().numpy()
