@@ -53,6 +53,8 @@ def _load():
         lib.oracle_scatter.restype = ctypes.c_int
         lib.oracle_gather.argtypes = [vp, vp, sz, i64, i64, i64, i64, i64]
         lib.oracle_gather.restype = ctypes.c_int
+        lib.oracle_linear.argtypes = [vp, vp, vp, i64, i64, i64]
+        lib.oracle_linear.restype = None
         lib.oracle_exchange_chunks.argtypes = [vp, vp, i64, i64]
         lib.oracle_exchange_chunks.restype = None
         lib.oracle_norm_rope_rows.argtypes = [vp, vp, i64, i64, vp, ctypes.c_double, vp, vp, i64, vp]
@@ -183,6 +185,62 @@ def fused_norm_rope_scatter(x_bits: np.ndarray, dtype: str, w_bits: np.ndarray, 
                             cos_tab: np.ndarray, sin_tab: np.ndarray) -> np.ndarray:
     """QK-norm -> RoPE -> head exchange, in that order; float64 head-sharded result."""
     return scatter(norm_rope_sharded(x_bits, dtype, w_bits, eps, cos_tab, sin_tab))
+
+
+# --------------------------------------------------------------------------
+# QKV projection ahead of the norm, rotation and exchange [QN "Description",
+# "Assumptions": projection -> QK-norm -> RoPE; every rank holds a token
+# shard and the full QKV weight].
+# --------------------------------------------------------------------------
+def linear(x64: np.ndarray, w64: np.ndarray) -> np.ndarray:
+    """y[m, n] = sum_k x[m, k] * w[n, k] in double (weight stored [out, in])."""
+    x64 = np.ascontiguousarray(x64, dtype=np.float64)
+    w64 = np.ascontiguousarray(w64, dtype=np.float64)
+    M, K = x64.shape
+    N, K2 = w64.shape
+    assert K == K2
+    y = np.empty((M, N), np.float64)
+    _load().oracle_linear(_p(x64), _p(w64), _p(y), M, N, K)
+    return y
+
+
+def qkv_proj_norm_rope_rows(x_rows: np.ndarray, dtype: str, w_qkv: np.ndarray, Hq: int, Hkv: int, D: int,
+                            wq_bits: np.ndarray, wk_bits: np.ndarray, eps: float, cos_tab: np.ndarray,
+                            sin_tab: np.ndarray, pos: np.ndarray):
+    """Projection, then QK-norm and RoPE at global positions `pos`, for token rows
+    x_rows[n, hidden] (16-bit storage).  The weight's output rows hold q's Hq*D
+    columns, then k's Hkv*D, then v's Hkv*D.  Returns float64 q [n, Hq, D],
+    k [n, Hkv, D] and v [n, Hkv, D] in source (token-major) layout."""
+    n, hidden = x_rows.shape
+    assert w_qkv.shape == ((Hq + 2 * Hkv) * D, hidden)
+    y = linear(widen(x_rows, dtype), widen(w_qkv, dtype))
+    q = y[:, :Hq * D].reshape(n, Hq, D)
+    k = y[:, Hq * D:(Hq + Hkv) * D].reshape(n, Hkv, D)
+    v = y[:, (Hq + Hkv) * D:].reshape(n, Hkv, D)
+    pos = np.asarray(pos, np.int64)
+
+    def nr(t, w_bits):
+        H = t.shape[1]
+        rows = norm_rope_rows(t.reshape(-1, D), widen(w_bits, dtype), eps, cos_tab, sin_tab,
+                              np.repeat(pos, H))
+        return rows.reshape(n, H, D)
+
+    return nr(q, wq_bits), nr(k, wk_bits), np.ascontiguousarray(v)
+
+
+def qkv_proj_norm_rope_scatter(x_bits: np.ndarray, dtype: str, w_qkv: np.ndarray, Hq: int, Hkv: int,
+                               wq_bits: np.ndarray, wk_bits: np.ndarray, eps: float, cos_tab: np.ndarray,
+                               sin_tab: np.ndarray):
+    """The whole front end for x_bits[P, B, S_l, hidden]: projection -> QK-norm ->
+    RoPE (positions r*S_l + s) -> head exchange.  float64 (q, k, v) head-sharded."""
+    P, B, S_l, hidden = x_bits.shape
+    D = w_qkv.shape[0] // (Hq + 2 * Hkv)
+    r = np.arange(P).reshape(P, 1, 1)
+    s = np.arange(S_l).reshape(1, 1, S_l)
+    pos = np.broadcast_to(r * S_l + s, (P, B, S_l)).reshape(-1)
+    q, k, v = qkv_proj_norm_rope_rows(x_bits.reshape(-1, hidden), dtype, w_qkv, Hq, Hkv, D, wq_bits, wk_bits,
+                                      eps, cos_tab, sin_tab, pos)
+    return tuple(scatter(t.reshape(P, B, S_l, t.shape[1], D)) for t in (q, k, v))
 
 
 # --------------------------------------------------------------------------

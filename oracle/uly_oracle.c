@@ -108,6 +108,26 @@ void oracle_exchange_chunks(const void *x_, void *y_, int64_t P, int64_t chunk_b
 }
 
 /* ------------------------------------------------------------------------
+ * QKV projection [QN "Description": the BF16 QKV projection heads the fused
+ * call; "Assumptions", exchange algorithm: every rank holds a token shard
+ * and the full QKV weight].  The weight is stored output-major, one row of
+ * `K` inputs per output column (the usual linear-layer layout):
+ *     y[m][n] = sum_k x[m][k] * w[n][k]
+ * x[M][K], w[N][K], y[M][N], all double (the 16-bit operands arrive
+ * widened exactly); no bias term, as the pages name none.
+ * ---------------------------------------------------------------------- */
+void oracle_linear(const double *x, const double *w, double *y, int64_t M, int64_t N, int64_t K)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += x[m * K + k] * w[n * K + k];
+            y[m * N + n] = acc;
+        }
+}
+
+/* ------------------------------------------------------------------------
  * Per-head RMSNorm then interleaved RoPE [QN "Assumptions"], one row of D
  * values per (token, head):
  *     ms   = (1/D) * sum_i x_i^2
