@@ -208,6 +208,32 @@ uly_status fused_qkv_norm_rope_scatter_packed(uly_ctx *ctx, const uly_tensor *q,
                                               int64_t table_rows, const char *tag, void *out,
                                               hipStream_t caller);
 
+/* The QKV projection ahead of the fused norm + RoPE scatter, in one launch
+ * ([QN "Description": the projection, the per-head RMSNorm of Q and K, the
+ * interleaved RoPE and the head exchange fused into one call per layer;
+ * "Assumptions": every rank holds a token shard and the full QKV weight,
+ * order projection -> QK-norm -> RoPE, fp32 math, 16-bit output]):
+ *     qkv[m][n] = sum_k x[m][k] * w_qkv[n][k]          (fp32 accumulation)
+ * then, per (token, head) row of q and k, the RMSNorm and rotation of
+ * fused_qk_norm_rope_scatter at global position r*S_l + s, one rounding,
+ * and the store into the head-sharded targets; v is rounded and stored.
+ *
+ * x:      [P][B][S_l][hidden] token rows, contiguous, rank-major.
+ * w_qkv:  [(Hq + 2*Hkv) * D][hidden], contiguous, output-major: rows
+ *         [0, Hq*D) project q (head h at rows h*D ...), then k's Hkv*D rows,
+ *         then v's.  No bias.
+ * dtype:  ULY_BF16 or ULY_F16 for x, w_qkv, w_q, w_k and the targets.
+ * D:      128 (the kernel's tile is one 128-wide head).
+ * hidden: a positive multiple of 32.  Hq, Hkv >= 1 and divisible by P.
+ * tags/outs: as for fused_qk_norm_rope_scatter; all three of q, k, v are
+ *         produced, into [B, P*S_l, Hq/P, D], [B, P*S_l, Hkv/P, D] twice.
+ * Runs on `caller`; the grouped handshake (uly_wait) covers it. */
+uly_status fused_qkv_proj_norm_rope_scatter(uly_ctx *ctx, const void *x, int dtype, int64_t B, int64_t S_l,
+                                           int64_t hidden, const void *w_qkv, int64_t Hq, int64_t Hkv, int64_t D,
+                                           const void *w_q, const void *w_k, float eps, const float *cos_tab,
+                                           const float *sin_tab, int64_t table_rows, const char *const tags[3],
+                                           void *const outs[3], hipStream_t caller);
+
 /* Grouped completion handshake ([P27 "Changes Made": one grouped handshake
  * for the tagged Q/K/V transfers]): make `consumer` wait, without any
  * host or device-wide synchronisation, for every scatter submitted since
@@ -291,7 +317,8 @@ typedef enum {
     ULY_K_GATHER = 2,        /* output relayout */
     ULY_K_PAD = 3,           /* sequence pad / trim */
     ULY_K_SPATIAL = 4,       /* spatial split / gather / concat */
-    ULY_K_COUNT = 5
+    ULY_K_PROJ = 5,          /* QKV projection with the norm + RoPE + scatter epilogue */
+    ULY_K_COUNT = 6
 } uly_kernel_kind;
 
 /* kind_mask bit k (1 << uly_kernel_kind) brackets launches of kind k with

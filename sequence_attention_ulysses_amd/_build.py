@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libuly.so")
-SOURCES = ["uly_kernels.hip", "uly_runtime.cpp"]
+SOURCES = ["uly_kernels.hip", "uly_proj.hip", "uly_runtime.cpp"]
 
 # Packed fp32 instructions are kept out of the generated code on purpose.
 HIPCC_FLAGS = [

@@ -35,14 +35,15 @@ MODE_GATHER = 1
 ROUTE_KERNEL = 0
 ROUTE_COPY_ENGINE = 1
 
-K_SCATTER, K_NORM_ROPE, K_GATHER, K_PAD, K_SPATIAL = range(5)
+K_SCATTER, K_NORM_ROPE, K_GATHER, K_PAD, K_SPATIAL, K_PROJ = range(6)
 KERNEL_KINDS = {"scatter": K_SCATTER, "norm_rope": K_NORM_ROPE, "gather": K_GATHER,
-                "pad": K_PAD, "spatial": K_SPATIAL}
+                "pad": K_PAD, "spatial": K_SPATIAL, "proj": K_PROJ}
 
 # Every symbol include/uly.h declares.
 EXPORTS = (
     "uly_create", "uly_destroy", "uly_target_register", "uly_target_lookup", "uly_target_count",
-    "ulysses_scatter_qkv", "fused_qk_norm_rope_scatter", "fused_qkv_norm_rope_scatter_packed", "uly_wait",
+    "ulysses_scatter_qkv", "fused_qk_norm_rope_scatter", "fused_qkv_norm_rope_scatter_packed",
+    "fused_qkv_proj_norm_rope_scatter", "uly_wait",
     "ulysses_gather_out", "uly_exchange_chunks",
     "uly_seq_pad_shard", "uly_seq_unshard_trim", "uly_spatial_split_halo",
     "uly_spatial_gather_stacked", "uly_spatial_trim_concat", "uly_rope_table_1d",
@@ -140,6 +141,8 @@ def load() -> ctypes.CDLL:
         "fused_qk_norm_rope_scatter": [vp, P_T, P_T, P_T, vp, vp, f32, vp, vp, i64, TAGS, OUTS, vp],
         "fused_qkv_norm_rope_scatter_packed": [vp, P_T, P_T, P_T, vp, vp, f32, vp, vp, i64, cp, vp, vp],
         "uly_exchange_chunks": [vp, vp, vp, i64, vp],
+        "fused_qkv_proj_norm_rope_scatter": [vp, vp, i32, i64, i64, i64, vp, i64, i64, i64, vp, vp, f32, vp, vp,
+                                             i64, TAGS, OUTS, vp],
         "uly_wait": [vp, vp],
         "ulysses_gather_out": [vp, P_T, cp, vp, vp],
         "uly_seq_pad_shard": [vp, vp, i32, i64, i64, i64, i64, vp, vp],

@@ -250,6 +250,45 @@ class UlyssesContext:
               "fused_qk_norm_rope_scatter")
         return dests
 
+    def fused_qkv_proj_norm_rope_scatter(self, x, w_qkv, Hq: int, Hkv: int, w_q, w_k, cos, sin, eps: float = 1e-6,
+                                         tags=("q", "k", "v"), out=None, stream=None):
+        """QKV projection + Q/K RMSNorm + RoPE + scatter, one launch on the caller's stream.
+
+        x: [P, B, S_l, hidden] token rows; w_qkv: [(Hq + 2*Hkv) * D, hidden] (q rows, then k,
+        then v; no bias); w_q, w_k: [D] norm weights; cos/sin: fp32 [rows >= P*S_l, D/2].
+        Returns the destination tensors (q, k, v), [P, B, P*S_l, H/P, D] each.
+        """
+        P = self.world_size
+        self._on_device(x, w_qkv, w_q, w_k, cos, sin)
+        if x.dim() != 4 or not x.is_contiguous() or not w_qkv.is_contiguous() or w_qkv.dim() != 2:
+            raise ValueError("x must be a contiguous [P, B, S_l, hidden] tensor and w_qkv a contiguous matrix")
+        if x.shape[0] != P:
+            raise ValueError("x must hold one slab per rank")
+        D = w_q.numel()
+        if w_qkv.shape != ((Hq + 2 * Hkv) * D, x.shape[3]) or w_qkv.dtype != x.dtype:
+            raise ValueError("w_qkv must be [(Hq + 2*Hkv) * D, hidden] in the activation dtype")
+        for w in (w_q, w_k):
+            if w.dtype != x.dtype or not w.is_contiguous() or w.numel() != D:
+                raise ValueError("norm weights must be contiguous [D] tensors in the activation dtype")
+        for t in (cos, sin):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2 or t.shape[1] * 2 != D:
+                raise ValueError("cos/sin tables must be contiguous fp32 [rows, D/2]")
+        B, S_l = x.shape[1], x.shape[2]
+        dests, ptrs = [], []
+        for i, H in enumerate((Hq, Hkv, Hkv)):
+            if H % P:
+                dests.append(None); ptrs.append(None)     # the library raises the precise error
+                continue
+            shape = (B, S_l * P, H // P, D)
+            o_i = None if out is None else out[i]
+            d, explicit = self._dest(tags[i], _lib.MODE_SCATTER, x, shape, o_i)
+            dests.append(d); ptrs.append(d.data_ptr() if explicit else None)
+        check(self._lib.fused_qkv_proj_norm_rope_scatter(
+            self._h(), x.data_ptr(), _dtype_code(x), B, S_l, x.shape[3], w_qkv.data_ptr(), Hq, Hkv, D,
+            w_q.data_ptr(), w_k.data_ptr(), float(eps), cos.data_ptr(), sin.data_ptr(), cos.shape[0],
+            _lib.tags_array(tags), _lib.ptr_array(ptrs), _stream_handle(stream)), "fused_qkv_proj_norm_rope_scatter")
+        return dests
+
     def fused_qkv_norm_rope_scatter_packed(self, q, k, v, w_q, w_k, cos, sin, eps: float = 1e-6, tag="qkv",
                                            out=None, stream=None):
         """Q/K norm + RoPE scatter with V into one packed target [P, B, P*S_l, H/P, 3*D]:

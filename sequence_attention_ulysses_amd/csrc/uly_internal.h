@@ -103,12 +103,42 @@ struct RowMapArgs {
     uint32_t pad;
 };
 
-// Launch wrappers (uly_kernels.hip).  They only enqueue; the caller checks
+// ---------------------------------------------------------------------------
+// QKV projection on MFMA with the Q/K norm + RoPE + head-band store epilogue
+// (uly_proj.hip).  x[M][K] holds the token rows of every rank, rank-major
+// (m = (r*B + b)*S_l + s); w[N][K] the weight, N = (Hq + 2*Hkv) * 128
+// output columns: q's heads, then k's, then v's.  A block computes one head
+// (128 columns) of kProjTileT tokens.
+// ---------------------------------------------------------------------------
+constexpr int kProjD = 128;          // head dim the projection kernel is built for
+constexpr int kProjThreads = 256;    // 4 waves
+constexpr int kProjTileT = 256;      // tokens per block (64 per wave)
+constexpr int kProjTileK = 32;       // K per LDS stage
+
+struct ProjArgs {
+    const uint16_t *x;
+    const uint16_t *w;
+    const uint16_t *wn[2];           // RMSNorm weights of q and k, [128]
+    uint16_t *dst[3];                // targets q, k, v: [P][B][S][Hl][128]
+    const float *cos_tab;            // [rows][64]
+    const float *sin_tab;
+    int64_t d_q[3], d_b[3], d_g[3];  // destination element strides (rank, batch, global token)
+    FastDiv sl;                      // S_l
+    FastDiv bdiv;                    // B
+    FastDiv hl[3];                   // heads per rank of q, k, v
+    FastDiv nh;                      // heads per token tile: Hq + 2*Hkv
+    uint32_t M, K, S_l;
+    uint32_t Hq, Hkv;
+    float eps, inv_D;
+};
+
+// Launch wrappers (uly_kernels.hip, uly_proj.hip).  They only enqueue; the caller checks
 // hipGetLastError().
 void launch_relayout(const CopyBatch &b, hipStream_t stream);
 void launch_norm_rope(const NormRopeArgs &a, int lanes, int dtype, bool uniform, bool tile, uint32_t blocks,
                       hipStream_t stream);
 void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
+void launch_proj(const ProjArgs &a, int dtype, uint32_t blocks, hipStream_t stream);
 
 #ifndef ULY_THREADS
 #define ULY_THREADS 256

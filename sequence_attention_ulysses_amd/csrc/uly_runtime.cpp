@@ -767,6 +767,93 @@ uly_status fused_qkv_norm_rope_scatter_packed(uly_ctx *c, const uly_tensor *q, c
     return fused_scatter(c, q, k, v, w_q, w_k, eps, cos_tab, sin_tab, table_rows, tags, outs, caller, true);
 }
 
+uly_status fused_qkv_proj_norm_rope_scatter(uly_ctx *c, const void *x, int dtype, int64_t B, int64_t S_l,
+                                           int64_t hidden, const void *w_qkv, int64_t Hq, int64_t Hkv, int64_t D,
+                                           const void *w_q, const void *w_k, float eps, const float *cos_tab,
+                                           const float *sin_tab, int64_t table_rows, const char *const tags[3],
+                                           void *const outs[3], hipStream_t caller) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    if (dtype != ULY_F16 && dtype != ULY_BF16) return fail(ULY_E_DTYPE, "the projection takes 16-bit floats");
+    if (B < 0 || S_l < 0) return fail(ULY_E_INVAL, "negative B or S_l");
+    if (Hq < 1 || Hkv < 1) return fail(ULY_E_INVAL, "q and k/v need at least one head each");
+    if (Hq % c->P != 0 || Hkv % c->P != 0)
+        return fail(ULY_E_INVAL, "heads (%lld, %lld) not divisible by world size %d", (long long)Hq,
+                    (long long)Hkv, c->P);
+    if (D != kProjD) return fail(ULY_E_UNSUPPORTED, "the projection kernel is built for head dim %d", kProjD);
+    if (hidden < kProjTileK || hidden % kProjTileK != 0)
+        return fail(ULY_E_INVAL, "hidden %lld is not a positive multiple of %d", (long long)hidden, kProjTileK);
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(ULY_E_INVAL, "eps must be a positive finite value");
+    const void *ptrs[4] = {x, w_qkv, w_q, w_k};
+    const char *pnames[4] = {"x", "w_qkv", "w_q", "w_k"};
+    for (int i = 0; i < 4; ++i)
+        if (!ptrs[i] || !aligned16(ptrs[i]))
+            return fail(ULY_E_INVAL, "%s: pointer null or not 16-byte aligned", pnames[i]);
+    if (!cos_tab || !sin_tab || !aligned16(cos_tab) || !aligned16(sin_tab))
+        return fail(ULY_E_INVAL, "cos/sin tables null or not 16-byte aligned");
+    if (table_rows < int64_t(c->P) * S_l)
+        return fail(ULY_E_INVAL, "table has %lld rows, positions reach %lld", (long long)table_rows,
+                    (long long)(int64_t(c->P) * S_l));
+    const int64_t M = int64_t(c->P) * B * S_l, N = (Hq + 2 * Hkv) * D;
+    const int64_t tiles = (M + kProjTileT - 1) / kProjTileT, NH = Hq + 2 * Hkv;
+    if (M >= (int64_t(1) << 31) || tiles * NH >= (int64_t(1) << 31) || hidden >= (int64_t(1) << 31))
+        return fail(ULY_E_UNSUPPORTED, "too large for one launch");
+    const char *names[3] = {"q", "k", "v"};
+    const int64_t heads[3] = {Hq, Hkv, Hkv};
+    uint8_t *dsts[3] = {nullptr, nullptr, nullptr};
+    std::vector<Range> in_ranges{byte_range(x, M * hidden * 2), byte_range(w_qkv, N * hidden * 2),
+                                 byte_range(w_q, D * 2), byte_range(w_k, D * 2),
+                                 byte_range(cos_tab, table_rows * (D / 2) * 4),
+                                 byte_range(sin_tab, table_rows * (D / 2) * 4)};
+    std::vector<Range> out_ranges;
+    for (int i = 0; i < 3; ++i) {
+        const int64_t tshape[4] = {B, S_l * c->P, heads[i] / c->P, D};
+        if ((st = resolve_target(c, names[i], tags ? tags[i] : nullptr, outs ? outs[i] : nullptr,
+                                 ULY_MODE_SCATTER, dtype, tshape, dsts[i])) != ULY_OK)
+            return st;
+        out_ranges.push_back(byte_range(dsts[i], int64_t(c->P) * tshape[0] * tshape[1] * tshape[2] * D * 2));
+    }
+    if ((st = check_overlaps(in_ranges, out_ranges)) != ULY_OK) return st;
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (out_ranges[i].overlaps(out_ranges[j]))
+                return fail(ULY_E_OVERLAP, "targets %s and %s overlap", names[i], names[j]);
+    if (c->host_only) return host_only_launch(c);
+    if (M == 0) return ULY_OK;
+
+    ProjArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = static_cast<const uint16_t *>(w_qkv);
+    a.wn[0] = static_cast<const uint16_t *>(w_q);
+    a.wn[1] = static_cast<const uint16_t *>(w_k);
+    a.cos_tab = cos_tab;
+    a.sin_tab = sin_tab;
+    const int64_t S = S_l * c->P;
+    for (int i = 0; i < 3; ++i) {
+        const int64_t Hl = heads[i] / c->P;
+        a.dst[i] = reinterpret_cast<uint16_t *>(dsts[i]);
+        a.d_q[i] = B * S * Hl * D;
+        a.d_b[i] = S * Hl * D;
+        a.d_g[i] = Hl * D;
+        a.hl[i] = FastDiv::make(uint32_t(Hl));
+    }
+    a.sl = FastDiv::make(uint32_t(S_l));
+    a.bdiv = FastDiv::make(uint32_t(B));
+    a.nh = FastDiv::make(uint32_t(NH));
+    a.M = uint32_t(M);
+    a.K = uint32_t(hidden);
+    a.S_l = uint32_t(S_l);
+    a.Hq = uint32_t(Hq);
+    a.Hkv = uint32_t(Hkv);
+    a.eps = eps;
+    a.inv_D = 1.0f / float(D);
+    const uint32_t blocks = uint32_t(tiles * NH);
+    DeviceGuard g(c->device);
+    if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
+    if ((st = launch(c, ULY_K_PROJ, caller, [&] { launch_proj(a, dtype, blocks, caller); })) != ULY_OK) return st;
+    return mark_pending(c, caller);
+}
+
 uly_status uly_wait(uly_ctx *c, hipStream_t consumer) {
     uly_status st = ctx_ok(c);
     if (st != ULY_OK) return st;

@@ -780,3 +780,93 @@ def test_exchange_chunks_bit_exact(dev, orc, P, chunk):
             yb = ctx.exchange_chunks(xb)
             torch.cuda.synchronize()
             np.testing.assert_array_equal(to_bits(yb), orc.exchange_chunks(to_bits(xb)))
+
+
+# ---------------------------------------------------------------------------
+# QKV projection (MFMA) with the norm + RoPE + scatter epilogue
+# ---------------------------------------------------------------------------
+def _proj_inputs(P, B, S_l, hidden, Hq, Hkv, dtype, seed, dev, D=128):
+    x = synth.normal((P, B, S_l, hidden), dtype, seed, dev)
+    w = synth.normal(((Hq + 2 * Hkv) * D, hidden), dtype, seed + 1, dev, std=hidden ** -0.5)
+    wq = synth.norm_weight(D, dtype, seed + 2, dev)
+    wk = synth.norm_weight(D, dtype, seed + 3, dev)
+    return x, w, wq, wk
+
+
+PROJ_SMALL = [
+    # P, B, S_l, hidden, Hq, Hkv, dtype
+    (2, 1, 40, 256, 4, 2, "bf16"),       # one ragged token tile
+    (4, 1, 200, 512, 8, 4, "bf16"),      # S_local = 200 tail, tiles cross rank boundaries
+    (1, 2, 33, 128, 2, 1, "f16"),
+    (4, 2, 64, 384, 4, 4, "bf16"),       # B = 2, twelve K stages
+    (8, 1, 32, 1024, 8, 8, "bf16"),
+    (2, 1, 300, 96, 2, 2, "f16"),        # three K stages
+]
+
+
+@pytest.mark.parametrize("P,B,S_l,hidden,Hq,Hkv,dtype", PROJ_SMALL)
+def test_projection_small(dev, orc, P, B, S_l, hidden, Hq, Hkv, dtype):
+    """flashinfer PR #6332, 'Description' / 'Assumptions': projection -> QK-norm -> RoPE ->
+    exchange, against the double-precision oracle element by element."""
+    x, w, wq, wk = _proj_inputs(P, B, S_l, hidden, Hq, Hkv, dtype, 60, dev)
+    rows = P * S_l + 3
+    cos, sin = rope_table_1d(rows, 128)
+    ocos, osin = orc.rope_table_1d(rows, 128)
+    with UlyssesContext(P, device=0) as ctx:
+        yq, yk, yv = ctx.fused_qkv_proj_norm_rope_scatter(x, w, Hq, Hkv, wq, wk, cos.to(dev), sin.to(dev))
+        ctx.wait()
+        torch.cuda.synchronize()
+        rq, rk, rv = orc.qkv_proj_norm_rope_scatter(to_bits(x), dtype, to_bits(w), Hq, Hkv, to_bits(wq),
+                                                    to_bits(wk), 1e-6, ocos, osin)
+        assert_close16(yq, rq, dtype, "q")
+        assert_close16(yk, rk, dtype, "k")
+        assert_close16(yv, rv, dtype, "v")
+        # deterministic: a second call gives the same bits
+        yq2, _, yv2 = ctx.fused_qkv_proj_norm_rope_scatter(x, w, Hq, Hkv, wq, wk, cos.to(dev), sin.to(dev),
+                                                           tags=("q2", "k2", "v2"))
+        torch.cuda.synchronize()
+        assert torch.equal(yq2.view(torch.int16), yq.view(torch.int16))
+        assert torch.equal(yv2.view(torch.int16), yv.view(torch.int16))
+
+
+def _check_proj_sampled(orc, x, w, wq, wk, ys, Hq, Hkv, dtype, cos, sin, windows):
+    """Oracle rows for sampled tokens of every rank, compared at their destinations."""
+    P, B, S_l, hidden = x.shape
+    toks = [(r, b, s) for r in range(P) for b in range(B) for (s0, n) in windows for s in range(s0, s0 + n)]
+    idx = torch.tensor([(r * B + b) * S_l + s for r, b, s in toks])
+    x_rows = to_bits(x.reshape(-1, hidden)[idx.to(x.device)])
+    pos = np.array([r * S_l + s for r, b, s in toks])
+    ref = orc.qkv_proj_norm_rope_rows(x_rows, dtype, to_bits(w), Hq, Hkv, 128, to_bits(wq), to_bits(wk), 1e-6,
+                                      cos, sin, pos)
+    for y, r_, H in zip(ys, ref, (Hq, Hkv, Hkv)):
+        Hl = H // P
+        h = torch.arange(H)
+        got = torch.stack([y[h // Hl, b, r * S_l + s, h % Hl] for r, b, s in toks])   # [n, H, D]
+        assert_close16(got, r_, dtype, "sampled")
+
+
+def test_projection_video_dit_full(dev, orc):
+    """Video-DiT block (P=4, S=16384, H=24, D=128, hidden 3072, bf16) at full size, the
+    launch the benchmark times; oracle rows on sampled token windows of every rank."""
+    P, B, S_l, H, hidden = 4, 1, 4096, 24, 3072
+    x, w, wq, wk = _proj_inputs(P, B, S_l, hidden, H, H, "bf16", 70, dev)
+    cos, sin = rope_table_1d(P * S_l, 128)
+    ocos, osin = orc.rope_table_1d(P * S_l, 128)
+    with UlyssesContext(P, device=0) as ctx:
+        ys = ctx.fused_qkv_proj_norm_rope_scatter(x, w, H, H, wq, wk, cos.to(dev), sin.to(dev))
+        ctx.wait()
+        torch.cuda.synchronize()
+        _check_proj_sampled(orc, x, w, wq, wk, ys, H, H, "bf16", ocos, osin, [(0, 3), (2047, 2), (4093, 3)])
+
+
+def test_projection_gqa_full(dev, orc):
+    """GQA (P=8, B=2, S_l=8192, Hq=32, Hkv=8, hidden 4096, bf16) at full size, sampled."""
+    P, B, S_l, Hq, Hkv, hidden = 8, 2, 8192, 32, 8, 4096
+    x, w, wq, wk = _proj_inputs(P, B, S_l, hidden, Hq, Hkv, "bf16", 80, dev)
+    cos, sin = rope_table_1d(P * S_l, 128)
+    ocos, osin = orc.rope_table_1d(P * S_l, 128)
+    with UlyssesContext(P, device=0) as ctx:
+        ys = ctx.fused_qkv_proj_norm_rope_scatter(x, w, Hq, Hkv, wq, wk, cos.to(dev), sin.to(dev))
+        ctx.wait()
+        torch.cuda.synchronize()
+        _check_proj_sampled(orc, x, w, wq, wk, ys, Hq, Hkv, "bf16", ocos, osin, [(0, 1), (8191, 1)])

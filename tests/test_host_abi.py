@@ -435,3 +435,47 @@ def test_exchange_chunks_checks(lib, ctx4):
     assert ex(ctx4.h, None, BASE, 16, None) == _lib.E_INVAL
     assert ex(ctx4.h, BASE, BASE + 16 * 4096 - 16, 4096, None) == _lib.E_OVERLAP   # 16 chunks of 4 KiB
     assert ex(ctx4.h, BASE, BASE + 16 * 4096, 4096, None) == _lib.E_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# QKV projection with the norm + RoPE + scatter epilogue
+# ---------------------------------------------------------------------------
+def _proj(lib, c, B=1, S_l=16, hidden=256, Hq=8, Hkv=4, D=128, dtype=_lib.BF16, x=BASE,
+          w=BASE + 32 * MiB, wn=(BASE + 200 * MiB, BASE + 201 * MiB), eps=1e-6, rows=64,
+          tabs=(BASE + 300 * MiB, BASE + 310 * MiB),
+          outs=(BASE + 100 * MiB, BASE + 120 * MiB, BASE + 140 * MiB), tags=("q", "k", "v")):
+    return lib.fused_qkv_proj_norm_rope_scatter(c.h, x, dtype, B, S_l, hidden, w, Hq, Hkv, D, wn[0], wn[1], eps,
+                                                tabs[0], tabs[1], rows, _lib.tags_array(tags),
+                                                _lib.ptr_array(outs), None)
+
+
+def test_projection_checks(lib, ctx4):
+    """flashinfer PR #6332, 'Description' / 'Assumptions': BF16 operands, head_dim 128,
+    heads divisible by the world size, rejected before any launch."""
+    assert _proj(lib, ctx4) == _lib.E_UNSUPPORTED and b"host-only" in lib.uly_last_error()
+    assert _proj(lib, ctx4, dtype=_lib.F16) == _lib.E_UNSUPPORTED
+    assert _proj(lib, ctx4, dtype=_lib.U8) == _lib.E_DTYPE
+    assert _proj(lib, ctx4, Hq=6) == _lib.E_INVAL and b"divisible" in lib.uly_last_error()
+    assert _proj(lib, ctx4, Hkv=2) == _lib.E_INVAL
+    assert _proj(lib, ctx4, Hkv=0) == _lib.E_INVAL
+    assert _proj(lib, ctx4, D=64) == _lib.E_UNSUPPORTED and b"head dim" in lib.uly_last_error()
+    assert _proj(lib, ctx4, hidden=48) == _lib.E_INVAL                     # not a multiple of 32
+    assert _proj(lib, ctx4, hidden=0) == _lib.E_INVAL
+    assert _proj(lib, ctx4, eps=0.0) == _lib.E_INVAL
+    assert _proj(lib, ctx4, x=BASE + 8) == _lib.E_INVAL                    # misaligned
+    assert _proj(lib, ctx4, w=0) == _lib.E_INVAL
+    assert _proj(lib, ctx4, wn=(BASE + 200 * MiB, 0)) == _lib.E_INVAL
+    assert _proj(lib, ctx4, rows=63) == _lib.E_INVAL                       # positions reach 64
+    assert _proj(lib, ctx4, B=-1) == _lib.E_INVAL
+    # x spans 4 * 16 * 256 * 2 bytes; a q target inside it is an overlap
+    assert _proj(lib, ctx4, outs=(BASE + 4096, BASE + 120 * MiB, BASE + 140 * MiB)) == _lib.E_OVERLAP
+    # targets must not overlap each other (q spans 4 * 64 * 2 * 128 * 2 bytes)
+    assert _proj(lib, ctx4, outs=(BASE + 100 * MiB, BASE + 100 * MiB + 4096, BASE + 140 * MiB)) == _lib.E_OVERLAP
+    # tagged targets: q [1, 64, 2, 128], k and v [1, 64, 1, 128]
+    tags = ("pq", "pk", "pv")
+    assert _proj(lib, ctx4, outs=(None, None, None), tags=tags) == _lib.E_NOT_FOUND
+    for i, (tag, hl) in enumerate(zip(tags, (2, 1, 1))):
+        assert register(lib, ctx4, tag, _lib.MODE_SCATTER, (1, 64, hl, 128), BASE + (100 + 20 * i) * MiB) == _lib.OK
+    assert _proj(lib, ctx4, outs=(None, None, None), tags=tags) == _lib.E_UNSUPPORTED
+    # an empty batch checks everything and launches nothing
+    assert _proj(lib, ctx4, B=0) == _lib.E_UNSUPPORTED
