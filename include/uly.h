@@ -224,7 +224,7 @@ uly_status fused_qkv_norm_rope_scatter_packed(uly_ctx *ctx, const uly_tensor *q,
  *         then v's.  No bias.
  * dtype:  ULY_BF16 or ULY_F16 for x, w_qkv, w_q, w_k and the targets.
  * D:      128 (the kernel's tile is one 128-wide head).
- * hidden: a positive multiple of 32.  Hq, Hkv >= 1 and divisible by P.
+ * hidden: a positive multiple of 64.  Hq, Hkv >= 1 and divisible by P.
  * tags/outs: as for fused_qk_norm_rope_scatter; all three of q, k, v are
  *         produced, into [B, P*S_l, Hq/P, D], [B, P*S_l, Hkv/P, D] twice.
  * Runs on `caller`; the grouped handshake (uly_wait) covers it. */

@@ -15,7 +15,7 @@ SOURCES = ["uly_kernels.hip", "uly_proj.hip", "uly_runtime.cpp"]
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wno-unused-command-line-argument", "-Wno-inline-asm",
 ]
 
 

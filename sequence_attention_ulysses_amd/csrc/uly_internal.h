@@ -108,12 +108,16 @@ struct RowMapArgs {
 // (uly_proj.hip).  x[M][K] holds the token rows of every rank, rank-major
 // (m = (r*B + b)*S_l + s); w[N][K] the weight, N = (Hq + 2*Hkv) * 128
 // output columns: q's heads, then k's, then v's.  A block computes one head
-// (128 columns) of kProjTileT tokens.
+// (128 columns each) of kProjHeads heads and kProjTileT tokens.
 // ---------------------------------------------------------------------------
 constexpr int kProjD = 128;          // head dim the projection kernel is built for
-constexpr int kProjThreads = 256;    // 4 waves
-constexpr int kProjTileT = 256;      // tokens per block (64 per wave)
-constexpr int kProjTileK = 32;       // K per LDS stage
+constexpr int kProjThreads = 256;    // 4 waves, 2 (heads) x 2 (tokens)
+constexpr int kProjHeads = 2;        // heads per block, one per wave row
+constexpr int kProjTileT = 256;      // tokens per block (128 per wave)
+#ifndef ULY_PROJ_TILE_K
+#define ULY_PROJ_TILE_K 64
+#endif
+constexpr int kProjTileK = ULY_PROJ_TILE_K;   // K per LDS stage
 
 struct ProjArgs {
     const uint16_t *x;
@@ -126,9 +130,9 @@ struct ProjArgs {
     FastDiv sl;                      // S_l
     FastDiv bdiv;                    // B
     FastDiv hl[3];                   // heads per rank of q, k, v
-    FastDiv nh;                      // heads per token tile: Hq + 2*Hkv
+    FastDiv nhb;                     // head blocks per token tile: ceil((Hq + 2*Hkv) / kProjHeads)
     uint32_t M, K, S_l;
-    uint32_t Hq, Hkv;
+    uint32_t Hq, Hkv, NH;            // NH = Hq + 2*Hkv
     float eps, inv_D;
 };
 

@@ -14,13 +14,21 @@
 // one lane's registers; one more exchange with lane ^ 32 turns the runs of 4
 // into 16-byte runs for the stores.
 //
-// Tiling: a block of 4 waves owns one head (128 output columns, one
-// component q, k or v) and 256 tokens; wave w owns tokens [64w, 64w+64), a
-// 128 x 64 tile of 4 x 2 MFMA blocks (128 fp32 accumulators per lane).  K
-// advances 32 at a time through a two-stage LDS ring; the global loads of
-// stage k+2 are in flight while stage k is multiplied.  LDS rows are 64
-// bytes (four 16-byte chunks) with the chunk index XOR-swizzled by row, so
-// the 16-byte fragment reads of 32 consecutive rows do not collide on banks.
+// Tiling: a block of 4 waves owns two heads (256 output columns; each head
+// is one component q, k or v) and 256 tokens.  Wave (wn, wt) owns head wn
+// and tokens [128wt, 128wt+128): a 128 x 128 tile of 4 x 4 MFMA blocks, 256
+// fp32 accumulators per lane (the AGPRs), so every 16-byte fragment read
+// from LDS feeds four products and one wave per SIMD is the occupancy.
+//
+// Operands go global -> LDS with global_load_lds_dwordx4 (no staging
+// registers, no ds_write) into a ring of K stages; the loads of later stages
+// are in flight while a stage is multiplied.  LDS rows are XOR-swizzled so
+// the 16-byte fragment reads do not collide on banks.
+//
+// Epilogue: the block's 256 cos/sin table rows are first staged into LDS in
+// one coalesced pass (as interleaved (cos, sin) pairs, rows padded by 16
+// bytes), so each rotation group reads its two (cos, sin) pairs with one
+// conflict-free 16-byte LDS read instead of dependent global loads.
 
 #include <hip/hip_runtime.h>
 
@@ -35,29 +43,115 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u32x4_t global_u32x4_t;
+typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kWaves = kProjThreads / 64;
 constexpr int kChunks = kProjTileK / 8;                  // 16-byte chunks per LDS row
-constexpr int kRowsA = kProjD;                           // weight rows per block
+constexpr int kRowsA = kProjHeads * kProjD;              // weight rows per block
 constexpr int kRowsB = kProjTileT;                       // token rows per block
-constexpr int kLoadsA = kRowsA * kChunks / kProjThreads; // 16-byte loads per thread per stage
-constexpr int kLoadsB = kRowsB * kChunks / kProjThreads;
-static_assert(kChunks == 4, "the LDS swizzle assumes 64-byte rows");
-static_assert(kRowsA * kChunks % kProjThreads == 0 && kRowsB * kChunks % kProjThreads == 0, "tile split");
-static_assert(kProjTileT == kWaves * 64, "each wave owns 64 tokens");
+constexpr int kWaveT = kProjTileT * kProjHeads / kWaves; // tokens per wave
+constexpr int kTB = kWaveT / 32;                         // 32-token MFMA blocks per wave
+static_assert(kChunks == 4 || kChunks == 8, "LDS rows of 64 or 128 bytes");
+static_assert(kWaves == kProjHeads * 2 && kWaveT == 128, "waves: 2 heads x 2 token halves of 128");
 
-__device__ __forceinline__ uint4 ldg16(const uint16_t *p) {
-    const u32x4_t v = *(const global_u32x4_t *)p;
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
+#ifndef ULY_PROJ_STAGES
+#define ULY_PROJ_STAGES 2
+#endif
+constexpr int kStages = ULY_PROJ_STAGES;
+static_assert(kStages >= 2, "a ring of at least two stages");
+constexpr int kSlotsA = kRowsA * kChunks, kSlotsB = kRowsB * kChunks;   // 16-byte slots per stage
+constexpr int kInstA = kSlotsA / 64 / kWaves, kInstB = kSlotsB / 64 / kWaves;   // loads per wave per stage
+static_assert(kSlotsA % (64 * kWaves) == 0 && kSlotsB % (64 * kWaves) == 0, "whole wave instructions");
+
+// The epilogue's table: per token, 64 (cos, sin) pairs = 32 chunks, plus one
+// chunk of padding so that 16 lanes reading the same chunk of 16 different
+// rows start 4 banks apart and cover the 64 banks once.
+constexpr int kTblRow = kProjD / 4 + 1;                  // 16-byte chunks per token row
+constexpr int kRingSlots = kStages * (kSlotsA + kSlotsB);
+constexpr int kTblSlots = kProjTileT * kTblRow;
+constexpr int kLdsSlots = kRingSlots > kTblSlots ? kRingSlots : kTblSlots;
+static_assert(kLdsSlots * 16 <= 160 * 1024, "LDS of one workgroup");
 
 __device__ __forceinline__ void stg16(uint16_t *p, uint4 v) {
     const u32x4_t w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, (global_u32x4_t *)p);
 }
 
-// LDS slot of 16-byte chunk c of row `row`.
-__device__ __forceinline__ int swz(int row, int c) { return row * kChunks + (c ^ ((row >> 1) & 3)); }
+__device__ __forceinline__ float4 ldg_f4(const float *p) {
+    const u32x4_t v = *(const global_u32x4_t *)p;
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
+// Workgroup barrier for LDS hand-offs only: this thread's LDS accesses are
+// complete, then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding global loads, so later stages' operand loads stay in flight
+// across it.  The memory clobber keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One 16-byte-per-lane global -> LDS load into the 64 slots starting at LDS
+// byte address `lds` (wave-uniform).  Issued as inline assembly so that the
+// compiler's wait insertion, which would otherwise make every later LDS read
+// wait for all such loads (including the stages still meant to be in
+// flight), leaves it alone: the kernel orders these loads itself with
+// wait_vmcnt before its barriers, and issues no other vector memory
+// instruction while any is outstanding.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VM) : "memory");
+}
+
+// Wait until at most min(N, later) stages of PER loads each are outstanding.
+template <int N, int PER>
+__device__ __forceinline__ void wait_stages(uint32_t later) {
+    if constexpr (N == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (later >= uint32_t(N)) wait_vmcnt<N * PER>();
+        else wait_stages<N - 1, PER>(later);
+    }
+}
+
+#ifndef ULY_PROJ_GROUP
+#define ULY_PROJ_GROUP 8
+#endif
+
+// Block -> (token tile, head block).  Workgroups go to the 8 XCDs round
+// robin (block b to XCD b % 8) and each XCD has its own L2.  The grid is cut
+// into 8 contiguous runs of logical blocks, one per XCD, and logical blocks
+// are ordered in groups of kGroupH head blocks x all token tiles (head
+// blocks fastest), so the ~32 blocks an XCD runs at once cover about 32 /
+// kGroupH token tiles and kGroupH head blocks: their X tiles and W slices
+// are shared in that XCD's L2 instead of streaming per block.  A bijection
+// for any grid size.
+constexpr uint32_t kGroupH = ULY_PROJ_GROUP;
+__device__ __forceinline__ void proj_block(const ProjArgs &a, uint32_t bid, uint32_t grid, uint32_t &tile,
+                                           uint32_t &hb) {
+    constexpr uint32_t kXcds = 8;
+    const uint32_t q = grid / kXcds, r = grid % kXcds;
+    const uint32_t x = bid % kXcds, k = bid / kXcds;
+    const uint32_t L = x * q + min(x, r) + k;
+    const uint32_t nhb = a.nhb.d, T = grid / nhb;
+    const uint32_t g = L / (kGroupH * T), rem = L % (kGroupH * T);
+    const uint32_t gh = min(kGroupH, nhb - g * kGroupH);
+    tile = rem / gh;
+    hb = g * kGroupH + rem % gh;
+}
+
+// LDS slot of 16-byte chunk c of row `row`.  The LDS serves a 16-byte read
+// of 16 lanes in one pass over 64 four-byte banks (256 bytes): 16
+// consecutive rows of 64 bytes span four bank sweeps of four rows each, so
+// rows r, r+4, r+8, r+12 must use four different chunk positions; rows of
+// 128 bytes sit two to a sweep, so eight rows share a set of positions.
+#ifndef ULY_PROJ_SWZ
+#define ULY_PROJ_SWZ (kChunks == 4 ? 2 : 1)
+#endif
+__device__ __forceinline__ int swz_key(int row) { return (row >> (ULY_PROJ_SWZ)) & (kChunks - 1); }
+__device__ __forceinline__ int swz(int row, int c) { return row * kChunks + (c ^ swz_key(row)); }
 
 template <int DT>
 __device__ __forceinline__ f32x16_t mfma(uint4 a, uint4 b, f32x16_t c) {
@@ -89,103 +183,76 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {   // one round to 
     }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kProjThreads) void proj_norm_rope_kernel(ProjArgs a) {
-    __shared__ uint4 sA[2][kRowsA * kChunks];
-    __shared__ uint4 sB[2][kRowsB * kChunks];
+// Global position of token row m (rank-major m = (r*B + b)*S_l + s) and its batch.
+__device__ __forceinline__ uint32_t token_pos(const ProjArgs &a, uint32_t m, uint32_t &b) {
+    uint32_t rb, s, r;
+    a.sl.divmod(m, rb, s);
+    a.bdiv.divmod(rb, r, b);
+    return r * a.S_l + s;
+}
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wv = tid >> 6;
-    uint32_t tile, hd;
-    a.nh.divmod(blockIdx.x, tile, hd);                  // heads fastest: a token tile stays hot in L2
-    const uint32_t m0 = tile * kProjTileT;
-    const uint16_t *wrow = a.w + size_t(hd) * kProjD * a.K;
-
-    // Global -> register staging of one K stage.  Rows past M read row M-1.
-    uint4 ra[kLoadsA], rb[kLoadsB];
-    auto gload = [&](uint32_t kt) {
-        const uint32_t k0 = kt * kProjTileK;
+// All threads of the block: the cos/sin rows of tokens m0 .. m0+255 (rows
+// past M repeat token M-1) into tbl[t][...], chunk j/2 of row t holding
+// (cos_j, sin_j, cos_j+1, sin_j+1) for even j.
+__device__ __forceinline__ void stage_table(const ProjArgs &a, uint32_t m0, float4 *tbl, int tid) {
+    constexpr int kPerRow = kProjD / 8;                  // float4 chunks of a cos (or sin) row
+    constexpr int kIter = kProjTileT * kPerRow / kProjThreads;
+    constexpr int kBatch = 8;
+    static_assert(kIter % kBatch == 0, "batches");
 #pragma unroll
-        for (int u = 0; u < kLoadsA; ++u) {
-            const int i = tid + u * kProjThreads;
-            ra[u] = ldg16(wrow + size_t(i / kChunks) * a.K + k0 + (i % kChunks) * 8);
+    for (int u0 = 0; u0 < kIter; u0 += kBatch) {
+        float4 c4[kBatch], s4[kBatch];
+        int row[kBatch], q[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int idx = tid + (u0 + u) * kProjThreads;
+            row[u] = idx / kPerRow;
+            q[u] = idx % kPerRow;
+            uint32_t b;
+            const uint32_t g = token_pos(a, min(m0 + uint32_t(row[u]), a.M - 1), b);
+            c4[u] = ldg_f4(a.cos_tab + size_t(g) * (kProjD / 2) + q[u] * 4);
+            s4[u] = ldg_f4(a.sin_tab + size_t(g) * (kProjD / 2) + q[u] * 4);
         }
 #pragma unroll
-        for (int u = 0; u < kLoadsB; ++u) {
-            const int i = tid + u * kProjThreads;
-            const uint32_t m = min(m0 + uint32_t(i / kChunks), a.M - 1);
-            rb[u] = ldg16(a.x + size_t(m) * a.K + k0 + (i % kChunks) * 8);
+        for (int u = 0; u < kBatch; ++u) {
+            tbl[row[u] * kTblRow + 2 * q[u]] = make_float4(c4[u].x, s4[u].x, c4[u].y, s4[u].y);
+            tbl[row[u] * kTblRow + 2 * q[u] + 1] = make_float4(c4[u].z, s4[u].z, c4[u].w, s4[u].w);
         }
-    };
-    auto sstore = [&](int st) {
-#pragma unroll
-        for (int u = 0; u < kLoadsA; ++u) {
-            const int i = tid + u * kProjThreads;
-            sA[st][swz(i / kChunks, i % kChunks)] = ra[u];
-        }
-#pragma unroll
-        for (int u = 0; u < kLoadsB; ++u) {
-            const int i = tid + u * kProjThreads;
-            sB[st][swz(i / kChunks, i % kChunks)] = rb[u];
-        }
-    };
-
-    f32x16_t acc[4][2];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
-
-    const uint32_t KT = a.K / kProjTileK;
-    gload(0);
-    sstore(0);
-    if (KT > 1) gload(1);
-    __syncthreads();
-    const int fr = lane & 31;          // fragment row (A) / column (B) of this lane
-    const int fk = lane >> 5;          // which 8-wide half of a 16-wide K step
-    for (uint32_t kt = 0; kt < KT; ++kt) {
-        const int st = kt & 1;
-        if (kt + 1 < KT) sstore(st ^ 1);   // stage kt+1, read back after the barrier below
-        if (kt + 2 < KT) gload(kt + 2);    // in flight during this stage's products
-#pragma unroll
-        for (int ks = 0; ks < kProjTileK / 16; ++ks) {
-            const int c = ks * 2 + fk;
-            uint4 fa[4], fb[2];
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) fa[nb] = sA[st][swz(nb * 32 + fr, c)];
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) fb[tb] = sB[st][swz(wv * 64 + tb * 32 + fr, c)];
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) acc[nb][tb] = mfma<DT>(fa[nb], fb[tb], acc[nb][tb]);
-        }
-        __syncthreads();
     }
+}
 
-    // ---- epilogue -----------------------------------------------------------
-    // acc[nb][tb][i] is column n = 32nb + 8(i/4) + 4*half + i%4 (the head-dim
-    // index d) of token 64wv + 32tb + lane%32.
+// The epilogue of wave (wn, wt): RMSNorm + RoPE of q/k rows (v as is), one
+// rounding, and the stores into the head-sharded targets.
+// acc[nb][tb][i] is column n = 32nb + 8(i/4) + 4*half + i%4 (the head-dim
+// index d) of token m0 + 128wt + 32tb + lane%32 and head `hd`.
+template <int DT>
+__device__ __forceinline__ void proj_epilogue(const ProjArgs &a, f32x16_t (&acc)[4][kTB], uint32_t m0,
+                                              uint32_t hd, int wt, int lane, const float4 *tbl) {
     const uint32_t half = lane >> 5;
     const int comp = hd < a.Hq ? 0 : (hd < a.Hq + a.Hkv ? 1 : 2);
     const uint32_t hc = hd - (comp == 0 ? 0u : (comp == 1 ? a.Hq : a.Hq + a.Hkv));
     uint32_t qd, jd;
     a.hl[comp].divmod(hc, qd, jd);
-    const uint16_t *wn = comp < 2 ? a.wn[comp] : nullptr;
     uint16_t *dbase = a.dst[comp] + int64_t(qd) * a.d_q[comp] + int64_t(jd) * kProjD;
     const int64_t d_b = a.d_b[comp], d_g = a.d_g[comp];
 
+    // this lane's 64 norm weights, d = 32nb + 8grp + 4half + 0..3, kept packed
+    uint2 wr[4][4];
+    if (comp < 2) {
+        const uint16_t *wn = a.wn[comp];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const uint32_t tok = m0 + wv * 64 + tb * 32 + (lane & 31);
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) wr[nb][grp] = *(const uint2 *)(wn + nb * 32 + grp * 8 + half * 4);
+    }
+
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) {
+        const int tl = wt * kWaveT + tb * 32 + (lane & 31);   // token within the block tile
+        const uint32_t tok = m0 + tl;
         const bool live = tok < a.M;
-        uint32_t rb_, s, r, b;
-        a.sl.divmod(live ? tok : a.M - 1, rb_, s);
-        a.bdiv.divmod(rb_, r, b);
-        const uint32_t g = r * a.S_l + s;
+        uint32_t b;
+        const uint32_t g = token_pos(a, live ? tok : a.M - 1, b);
         float inv = 1.f;
         if (comp < 2) {
             float ss = 0.f;
@@ -198,26 +265,22 @@ __global__ __launch_bounds__(kProjThreads) void proj_norm_rope_kernel(ProjArgs a
             inv = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_D, a.eps));
         }
         uint16_t *drow = dbase + int64_t(b) * d_b + int64_t(g) * d_g;
-        const float *crow = a.cos_tab + size_t(g) * (kProjD / 2);
-        const float *srow = a.sin_tab + size_t(g) * (kProjD / 2);
+        const float4 *trow = tbl + tl * kTblRow;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             uint32_t pk[8];   // pk[2*grp + p]: the pair (d0 + 2p, d0 + 2p + 1) of register group grp
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
-                const int d0 = nb * 32 + grp * 8 + int(half) * 4;
                 if (comp < 2) {
-                    const float2 cc = *(const float2 *)(crow + d0 / 2);
-                    const float2 sn = *(const float2 *)(srow + d0 / 2);
-                    const uint2 wr = *(const uint2 *)(wn + d0);
-                    const float wf[4] = {widen1<DT>(wr.x & 0xFFFFu), widen1<DT>(wr.x >> 16),
-                                         widen1<DT>(wr.y & 0xFFFFu), widen1<DT>(wr.y >> 16)};
-                    const float cv[2] = {cc.x, cc.y}, sv[2] = {sn.x, sn.y};
+                    // pairs j0 = 16nb + 4grp + 2half and j0 + 1: chunk j0 / 2 of the row
+                    const float4 cs = trow[nb * 8 + grp * 2 + half];
+                    const float cv[2] = {cs.x, cs.z}, sv[2] = {cs.y, cs.w};
+                    const uint32_t wp[2] = {wr[nb][grp].x, wr[nb][grp].y};
 #pragma unroll
                     for (int p = 0; p < 2; ++p) {
                         const int i0 = grp * 4 + p * 2;
-                        const float n0 = acc[nb][tb][i0] * inv * wf[2 * p];
-                        const float n1 = acc[nb][tb][i0 + 1] * inv * wf[2 * p + 1];
+                        const float n0 = acc[nb][tb][i0] * inv * widen1<DT>(wp[p] & 0xFFFFu);
+                        const float n1 = acc[nb][tb][i0 + 1] * inv * widen1<DT>(wp[p] >> 16);
                         pk[grp * 2 + p] = pack2<DT>(n0 * cv[p] - n1 * sv[p], n0 * sv[p] + n1 * cv[p]);
                     }
                 } else {
@@ -246,13 +309,114 @@ __global__ __launch_bounds__(kProjThreads) void proj_norm_rope_kernel(ProjArgs a
     }
 }
 
+// 256 accumulators per lane leave room for one wave per SIMD; saying so keeps
+// the scheduler from trading latency hiding for an occupancy it cannot reach.
+template <int DT>
+__global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void proj_kernel(ProjArgs a) {
+    __shared__ uint4 lds[kLdsSlots];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int wn = wv >> 1;            // head of the block this wave computes
+    const int wt = wv & 1;             // token half of the block this wave computes
+    uint32_t tile, hb;
+    proj_block(a, blockIdx.x, gridDim.x, tile, hb);
+    const uint32_t m0 = tile * kProjTileT;
+    const uint32_t head0 = hb * kProjHeads;
+    const uint32_t last_row = a.NH * kProjD - 1;        // an odd head count leaves the last block half empty
+
+    // Per lane: the global 16-byte chunk of the slot it fills in each of its
+    // load instructions (the same for every stage; only k moves).  Rows past
+    // M read row M-1, weight rows past the last head the last row; neither is
+    // stored.  The host keeps N*K/8 and M*K/8 below 2^31.
+    const uint4 *wq = reinterpret_cast<const uint4 *>(a.w), *xq = reinterpret_cast<const uint4 *>(a.x);
+    const uint32_t K8 = a.K / 8;
+    uint32_t offA[kInstA], offB[kInstB];
+#pragma unroll
+    for (int u = 0; u < kInstA; ++u) {
+        const int slot = (wv * kInstA + u) * 64 + lane;
+        const int row = slot / kChunks, c = (slot % kChunks) ^ swz_key(row);
+        offA[u] = min(head0 * kProjD + uint32_t(row), last_row) * K8 + c;
+    }
+#pragma unroll
+    for (int u = 0; u < kInstB; ++u) {
+        const int slot = (wv * kInstB + u) * 64 + lane;
+        const int row = slot / kChunks, c = (slot % kChunks) ^ swz_key(row);
+        offB[u] = min(m0 + uint32_t(row), a.M - 1) * K8 + c;
+    }
+    // LDS byte addresses (wave-uniform): the ring base and this wave's first
+    // slot in the A and the B region of a stage.
+    const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)(&lds[0]));
+    const uint32_t wu = __builtin_amdgcn_readfirstlane(uint32_t(wv));
+    const uint32_t wA = wu * kInstA * 64 * 16;
+    const uint32_t wB = kSlotsA * 16 + wu * kInstB * 64 * 16;
+    auto issue = [&](uint32_t kt, uint32_t st) {
+        const uint32_t k0 = kt * (kProjTileK / 8);
+        const uint32_t sb = ring + st * (kSlotsA + kSlotsB) * 16;
+#pragma unroll
+        for (int u = 0; u < kInstA; ++u) dma16(wq + offA[u] + k0, sb + wA + u * 64 * 16);
+#pragma unroll
+        for (int u = 0; u < kInstB; ++u) dma16(xq + offB[u] + k0, sb + wB + u * 64 * 16);
+    };
+
+    f32x16_t acc[4][kTB];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < kTB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
+
+    const uint32_t KT = a.K / kProjTileK;
+#pragma unroll
+    for (int p = 0; p < kStages - 1; ++p)
+        if (uint32_t(p) < KT) issue(p, p);
+    const int fr = lane & 31;          // fragment row (A) / column (B) of this lane
+    const int fk = lane >> 5;          // which 8-wide half of a 16-wide K step
+    constexpr int kPer = kInstA + kInstB;
+    for (uint32_t kt = 0; kt < KT; ++kt) {
+        const uint32_t st = kt % kStages;
+        // this wave's loads of stage kt are done once at most the later
+        // stages' loads (kt+1 .. kt+kStages-2 where they exist) are outstanding
+        wait_stages<kStages - 2, kPer>(KT - 1 - kt);
+        lds_barrier();     // every wave's stage kt landed; every wave is done with stage kt-1
+        if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
+        const uint4 *sa = lds + st * (kSlotsA + kSlotsB), *sb = sa + kSlotsA;
+#pragma unroll
+        for (int ks = 0; ks < kProjTileK / 16; ++ks) {
+            const int c = ks * 2 + fk;
+            uint4 fa[4], fb[kTB];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) fa[nb] = sa[swz(wn * kProjD + nb * 32 + fr, c)];
+#pragma unroll
+            for (int tb = 0; tb < kTB; ++tb) fb[tb] = sb[swz(wt * kWaveT + tb * 32 + fr, c)];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int tb = 0; tb < kTB; ++tb) acc[nb][tb] = mfma<DT>(fa[nb], fb[tb], acc[nb][tb]);
+        }
+    }
+
+    // The ring is free once every wave is past its last stage: stage the
+    // block's table rows there (only blocks with a q or k head rotate).
+    float4 *tbl = reinterpret_cast<float4 *>(lds);
+    lds_barrier();
+    if (head0 < a.Hq + a.Hkv) {
+        stage_table(a, m0, tbl, tid);
+        lds_barrier();
+    }
+    const uint32_t hd = head0 + wn;
+    if (hd < a.NH) proj_epilogue<DT>(a, acc, m0, hd, wt, lane, tbl);
+}
+
 }  // namespace
 
 void launch_proj(const ProjArgs &a, int dtype, uint32_t blocks, hipStream_t stream) {
     if (dtype == ULY_BF16)
-        hipLaunchKernelGGL(proj_norm_rope_kernel<2>, dim3(blocks), dim3(kProjThreads), 0, stream, a);
+        hipLaunchKernelGGL(proj_kernel<2>, dim3(blocks), dim3(kProjThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(proj_norm_rope_kernel<1>, dim3(blocks), dim3(kProjThreads), 0, stream, a);
+        hipLaunchKernelGGL(proj_kernel<1>, dim3(blocks), dim3(kProjThreads), 0, stream, a);
 }
 
 }  // namespace uly

@@ -796,7 +796,9 @@ uly_status fused_qkv_proj_norm_rope_scatter(uly_ctx *c, const void *x, int dtype
                     (long long)(int64_t(c->P) * S_l));
     const int64_t M = int64_t(c->P) * B * S_l, N = (Hq + 2 * Hkv) * D;
     const int64_t tiles = (M + kProjTileT - 1) / kProjTileT, NH = Hq + 2 * Hkv;
-    if (M >= (int64_t(1) << 31) || tiles * NH >= (int64_t(1) << 31) || hidden >= (int64_t(1) << 31))
+    const int64_t NHB = (NH + kProjHeads - 1) / kProjHeads;
+    if (M >= (int64_t(1) << 31) || tiles * NHB >= (int64_t(1) << 31) || hidden >= (int64_t(1) << 31) ||
+        M * hidden / 8 >= (int64_t(1) << 31) || N * hidden / 8 >= (int64_t(1) << 31))
         return fail(ULY_E_UNSUPPORTED, "too large for one launch");
     const char *names[3] = {"q", "k", "v"};
     const int64_t heads[3] = {Hq, Hkv, Hkv};
@@ -839,7 +841,8 @@ uly_status fused_qkv_proj_norm_rope_scatter(uly_ctx *c, const void *x, int dtype
     }
     a.sl = FastDiv::make(uint32_t(S_l));
     a.bdiv = FastDiv::make(uint32_t(B));
-    a.nh = FastDiv::make(uint32_t(NH));
+    a.nhb = FastDiv::make(uint32_t(NHB));
+    a.NH = uint32_t(NH);
     a.M = uint32_t(M);
     a.K = uint32_t(hidden);
     a.S_l = uint32_t(S_l);
@@ -847,7 +850,7 @@ uly_status fused_qkv_proj_norm_rope_scatter(uly_ctx *c, const void *x, int dtype
     a.Hkv = uint32_t(Hkv);
     a.eps = eps;
     a.inv_D = 1.0f / float(D);
-    const uint32_t blocks = uint32_t(tiles * NH);
+    const uint32_t blocks = uint32_t(tiles * NHB);
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
     if ((st = launch(c, ULY_K_PROJ, caller, [&] { launch_proj(a, dtype, blocks, caller); })) != ULY_OK) return st;

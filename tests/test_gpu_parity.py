@@ -798,9 +798,9 @@ PROJ_SMALL = [
     (2, 1, 40, 256, 4, 2, "bf16"),       # one ragged token tile
     (4, 1, 200, 512, 8, 4, "bf16"),      # S_local = 200 tail, tiles cross rank boundaries
     (1, 2, 33, 128, 2, 1, "f16"),
-    (4, 2, 64, 384, 4, 4, "bf16"),       # B = 2, twelve K stages
+    (4, 2, 64, 384, 4, 4, "bf16"),       # B = 2, six K stages
     (8, 1, 32, 1024, 8, 8, "bf16"),
-    (2, 1, 300, 96, 2, 2, "f16"),        # three K stages
+    (2, 1, 300, 192, 2, 2, "f16"),       # three K stages
 ]
 
 

@@ -459,7 +459,7 @@ def test_projection_checks(lib, ctx4):
     assert _proj(lib, ctx4, Hkv=2) == _lib.E_INVAL
     assert _proj(lib, ctx4, Hkv=0) == _lib.E_INVAL
     assert _proj(lib, ctx4, D=64) == _lib.E_UNSUPPORTED and b"head dim" in lib.uly_last_error()
-    assert _proj(lib, ctx4, hidden=48) == _lib.E_INVAL                     # not a multiple of 32
+    assert _proj(lib, ctx4, hidden=96) == _lib.E_INVAL                     # not a multiple of 64
     assert _proj(lib, ctx4, hidden=0) == _lib.E_INVAL
     assert _proj(lib, ctx4, eps=0.0) == _lib.E_INVAL
     assert _proj(lib, ctx4, x=BASE + 8) == _lib.E_INVAL                    # misaligned
