@@ -110,10 +110,14 @@ struct RowMapArgs {
 // output columns: q's heads, then k's, then v's.  A block computes one head
 // (128 columns each) of kProjHeads heads and kProjTileT tokens.
 // ---------------------------------------------------------------------------
+#ifndef ULY_PROJ_WAVE_T
+#define ULY_PROJ_WAVE_T 64
+#endif
 constexpr int kProjD = 128;          // head dim the projection kernel is built for
-constexpr int kProjThreads = 256;    // 4 waves, 2 (heads) x 2 (tokens)
 constexpr int kProjHeads = 2;        // heads per block, one per wave row
-constexpr int kProjTileT = 256;      // tokens per block (128 per wave)
+constexpr int kProjTileT = 256;      // tokens per block
+constexpr int kProjWaveT = ULY_PROJ_WAVE_T;                            // tokens per wave
+constexpr int kProjThreads = kProjHeads * (kProjTileT / kProjWaveT) * 64;   // 8 waves (4 for 128)
 #ifndef ULY_PROJ_TILE_K
 #define ULY_PROJ_TILE_K 64
 #endif

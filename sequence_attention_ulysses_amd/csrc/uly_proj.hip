@@ -14,11 +14,13 @@
 // one lane's registers; one more exchange with lane ^ 32 turns the runs of 4
 // into 16-byte runs for the stores.
 //
-// Tiling: a block of 4 waves owns two heads (256 output columns; each head
+// Tiling: a block of 8 waves owns two heads (256 output columns; each head
 // is one component q, k or v) and 256 tokens.  Wave (wn, wt) owns head wn
-// and tokens [128wt, 128wt+128): a 128 x 128 tile of 4 x 4 MFMA blocks, 256
-// fp32 accumulators per lane (the AGPRs), so every 16-byte fragment read
-// from LDS feeds four products and one wave per SIMD is the occupancy.
+// and tokens [64wt, 64wt+64): a 128 x 64 tile of 4 x 2 MFMA blocks, 128
+// fp32 accumulators per lane, so two waves fit on each SIMD and one wave's
+// epilogue and barriers overlap the other's products.  (128-token waves,
+// 256 accumulators and one wave per SIMD, read less LDS per product but
+// leave the matrix cores idle through every epilogue; measured slower.)
 //
 // Operands go global -> LDS with global_load_lds_dwordx4 (no staging
 // registers, no ds_write) into a ring of K stages; the loads of later stages
@@ -49,10 +51,12 @@ constexpr int kWaves = kProjThreads / 64;
 constexpr int kChunks = kProjTileK / 8;                  // 16-byte chunks per LDS row
 constexpr int kRowsA = kProjHeads * kProjD;              // weight rows per block
 constexpr int kRowsB = kProjTileT;                       // token rows per block
-constexpr int kWaveT = kProjTileT * kProjHeads / kWaves; // tokens per wave
+constexpr int kWaveT = kProjWaveT;                       // tokens per wave
 constexpr int kTB = kWaveT / 32;                         // 32-token MFMA blocks per wave
+constexpr int kWavesT = kProjTileT / kWaveT;             // waves along the tokens
+constexpr int kWavesPerSimd = kWaves / 4;                // occupancy: one block per CU
 static_assert(kChunks == 4 || kChunks == 8, "LDS rows of 64 or 128 bytes");
-static_assert(kWaves == kProjHeads * 2 && kWaveT == 128, "waves: 2 heads x 2 token halves of 128");
+static_assert(kWaves == kProjHeads * kWavesT && (kWaveT == 64 || kWaveT == 128), "wave grid");
 
 #ifndef ULY_PROJ_STAGES
 #define ULY_PROJ_STAGES 2
@@ -72,9 +76,16 @@ constexpr int kTblSlots = kProjTileT * kTblRow;
 constexpr int kLdsSlots = kRingSlots > kTblSlots ? kRingSlots : kTblSlots;
 static_assert(kLdsSlots * 16 <= 160 * 1024, "LDS of one workgroup");
 
+#ifndef ULY_PROJ_NT_STORE
+#define ULY_PROJ_NT_STORE 0
+#endif
+// Output stores.  A store instruction writes 32-byte pieces of 32 rows, so
+// the pieces of one line arrive from several instructions: ordinary stores
+// let the L2 merge them into whole lines before they go out.
 __device__ __forceinline__ void stg16(uint16_t *p, uint4 v) {
     const u32x4_t w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, (global_u32x4_t *)p);
+    if (ULY_PROJ_NT_STORE) __builtin_nontemporal_store(w, (global_u32x4_t *)p);
+    else *(global_u32x4_t *)p = w;
 }
 
 __device__ __forceinline__ float4 ldg_f4(const float *p) {
@@ -117,8 +128,12 @@ __device__ __forceinline__ void wait_stages(uint32_t later) {
 }
 
 #ifndef ULY_PROJ_GROUP
-#define ULY_PROJ_GROUP 8
+#define ULY_PROJ_GROUP 4
 #endif
+#ifndef ULY_PROJ_SPREAD
+#define ULY_PROJ_SPREAD 1
+#endif
+constexpr bool kSpread = ULY_PROJ_SPREAD;
 
 // Block -> (token tile, head block).  Workgroups go to the 8 XCDs round
 // robin (block b to XCD b % 8) and each XCD has its own L2.  The grid is cut
@@ -197,7 +212,10 @@ __device__ __forceinline__ uint32_t token_pos(const ProjArgs &a, uint32_t m, uin
 __device__ __forceinline__ void stage_table(const ProjArgs &a, uint32_t m0, float4 *tbl, int tid) {
     constexpr int kPerRow = kProjD / 8;                  // float4 chunks of a cos (or sin) row
     constexpr int kIter = kProjTileT * kPerRow / kProjThreads;
-    constexpr int kBatch = 8;
+#ifndef ULY_PROJ_TBL_BATCH
+#define ULY_PROJ_TBL_BATCH 8
+#endif
+    constexpr int kBatch = ULY_PROJ_TBL_BATCH;
     static_assert(kIter % kBatch == 0, "batches");
 #pragma unroll
     for (int u0 = 0; u0 < kIter; u0 += kBatch) {
@@ -309,17 +327,18 @@ __device__ __forceinline__ void proj_epilogue(const ProjArgs &a, f32x16_t (&acc)
     }
 }
 
-// 256 accumulators per lane leave room for one wave per SIMD; saying so keeps
-// the scheduler from trading latency hiding for an occupancy it cannot reach.
+// The occupancy is fixed by the LDS (one block per CU); saying so keeps the
+// scheduler from trading latency hiding for an occupancy it cannot reach.
 template <int DT>
-__global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void proj_kernel(ProjArgs a) {
+__global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
+void proj_kernel(ProjArgs a) {
     __shared__ uint4 lds[kLdsSlots];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
-    const int wn = wv >> 1;            // head of the block this wave computes
-    const int wt = wv & 1;             // token half of the block this wave computes
+    const int wn = wv / kWavesT;       // head of the block this wave computes
+    const int wt = wv % kWavesT;       // token slice of the block this wave computes
     uint32_t tile, hb;
     proj_block(a, blockIdx.x, gridDim.x, tile, hb);
     const uint32_t m0 = tile * kProjTileT;
@@ -351,13 +370,16 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(1,
     const uint32_t wu = __builtin_amdgcn_readfirstlane(uint32_t(wv));
     const uint32_t wA = wu * kInstA * 64 * 16;
     const uint32_t wB = kSlotsA * 16 + wu * kInstB * 64 * 16;
-    auto issue = [&](uint32_t kt, uint32_t st) {
+    // Part `part` of `parts` of the loads of stage kt into ring slot st.
+    auto issue = [&](uint32_t kt, uint32_t st, int part, int parts) {
         const uint32_t k0 = kt * (kProjTileK / 8);
         const uint32_t sb = ring + st * (kSlotsA + kSlotsB) * 16;
 #pragma unroll
-        for (int u = 0; u < kInstA; ++u) dma16(wq + offA[u] + k0, sb + wA + u * 64 * 16);
+        for (int u = 0; u < kInstA; ++u)
+            if (u * parts / kInstA == part) dma16(wq + offA[u] + k0, sb + wA + u * 64 * 16);
 #pragma unroll
-        for (int u = 0; u < kInstB; ++u) dma16(xq + offB[u] + k0, sb + wB + u * 64 * 16);
+        for (int u = 0; u < kInstB; ++u)
+            if (u * parts / kInstB == part) dma16(xq + offB[u] + k0, sb + wB + u * 64 * 16);
     };
 
     f32x16_t acc[4][kTB];
@@ -371,7 +393,7 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(1,
     const uint32_t KT = a.K / kProjTileK;
 #pragma unroll
     for (int p = 0; p < kStages - 1; ++p)
-        if (uint32_t(p) < KT) issue(p, p);
+        if (uint32_t(p) < KT) issue(p, p, 0, 1);
     const int fr = lane & 31;          // fragment row (A) / column (B) of this lane
     const int fk = lane >> 5;          // which 8-wide half of a 16-wide K step
     constexpr int kPer = kInstA + kInstB;
@@ -381,7 +403,9 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(1,
         // stages' loads (kt+1 .. kt+kStages-2 where they exist) are outstanding
         wait_stages<kStages - 2, kPer>(KT - 1 - kt);
         lds_barrier();     // every wave's stage kt landed; every wave is done with stage kt-1
-        if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
+        const bool more = kt + kStages - 1 < KT;
+        const uint32_t kn = kt + kStages - 1, sn = (kt + kStages - 1) % kStages;
+        if (!kSpread && more) issue(kn, sn, 0, 1);
         const uint4 *sa = lds + st * (kSlotsA + kSlotsB), *sb = sa + kSlotsA;
 #pragma unroll
         for (int ks = 0; ks < kProjTileK / 16; ++ks) {
@@ -391,6 +415,8 @@ __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(1,
             for (int nb = 0; nb < 4; ++nb) fa[nb] = sa[swz(wn * kProjD + nb * 32 + fr, c)];
 #pragma unroll
             for (int tb = 0; tb < kTB; ++tb) fb[tb] = sb[swz(wt * kWaveT + tb * 32 + fr, c)];
+            // the next stage's loads, spread over the K steps between the products
+            if (kSpread && more) issue(kn, sn, ks, kProjTileK / 16);
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
