@@ -230,8 +230,91 @@ def setup_spatial(torch, dev, synth, rope_table_1d, UlyssesContext):
                        "bytes_per_step": split + gather + trim, "note": "cache-resident"}}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def setup_video_dit_proj(torch, dev, synth, rope_table_1d, UlyssesContext):
+    """The attention front end with the QKV projection fused in: one launch
+    projects x, normalises and rotates q/k and stores every head band into
+    its head-sharded target (flashinfer PR #6332's fused call), then the wait
+    and the output gather.  Timed beside it: the per-operator path, a library
+    GEMM (torch, hipBLASLt) writing qkv, then the fused norm/RoPE scatter."""
+    import torch.nn.functional as F
+    w = synth.VIDEO_DIT
+    P, B, S_l, H, D = w.P, w.B, w.S_l, w.Hq, w.D
+    hidden, N = H * D, 3 * H * D
+    M = P * B * S_l
+    x = synth.normal((P, B, S_l, hidden), "bf16", 70, dev)
+    w_qkv = synth.normal((N, hidden), "bf16", 71, dev, std=hidden ** -0.5)
+    w_q, w_k = synth.norm_weight(D, "bf16", 72, dev), synth.norm_weight(D, "bf16", 73, dev)
+    cos, sin = (t.to(dev) for t in rope_table_1d(P * S_l, D, theta=w.theta))
+    o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 74, dev)
+    ctx = UlyssesContext(P, device=0)
+    flops = 2 * M * N * hidden
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    yv = y.view(P, B, S_l, 3, H, D)
+    x2 = x.view(M, hidden)
+
+    def step():
+        ctx.fused_qkv_proj_norm_rope_scatter(x, w_qkv, H, H, w_q, w_k, cos, sin, eps=w.eps)
+        ctx.wait()
+        ctx.gather_out(o)
+
+    def step_per_operator():
+        F.linear(x2, w_qkv, out=y)
+        ctx.fused_qk_norm_rope_scatter(yv[:, :, :, 0], yv[:, :, :, 1], w_q, w_k, cos, sin, eps=w.eps,
+                                       v=yv[:, :, :, 2], tags=("pq", "pk", "pv"))
+        ctx.wait()
+        ctx.gather_out(o)
+
+    return {"workload": w, "name": "video_dit_proj_p4_s16384_h24_hidden3072_bf16", "ctx": ctx, "step": step,
+            "step_per_operator": step_per_operator,
+            "bytes_per_step": flops, "unit": "TFLOP/s", "unit_div": 1e12,
+            "metric": "QKV projection + QK-norm + RoPE + Ulysses scatter + output gather, projection TFLOP/s "
+                      "over the step, P=4 bf16, 1 MI355X",
+            "dominant": ("proj", flops, "proj_kernel<bf16> (MFMA QKV projection with norm/RoPE/band-store "
+                         "epilogue)", "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"),
+            "cpu_proj": (x, w_qkv, w_q, w_k, H, w.eps, w.theta),
+            "dtype": "bf16", "data": "synthetic N(0,1) activations, N(0,1/hidden) QKV weight, N(1,0.1) norm "
+                                     "weights, 1-D RoPE theta 1e4 (seeded)",
+            "config": {"workload": "video_dit_proj_p4_s16384_h24_hidden3072_bf16", "P": P, "B": B, "S_local": S_l,
+                       "S": P * S_l, "H": H, "D": D, "hidden": hidden, "M": M, "N": N,
+                       "flops_per_step": flops, "parallelism": "ulysses-p4-emulated"}}
+
+
+def cpu_baseline_proj(args, proj_inputs, min_seconds: float = 10.0):
+    """The CPU oracle on a bounded sample of the projection workload: the
+    projection, QK-norm and RoPE of 16 token rows at a time, repeated for
+    about `min_seconds`; the rate counts the projection's flops."""
+    import numpy as np
+
+    from oracle import oracle
+    from sequence_attention_ulysses_amd import synth
+
+    x, w_qkv, w_q, w_k, H, eps, theta = proj_inputs
+    P, B, S_l, hidden = x.shape
+    D = w_q.numel()
+    xb, wb = synth.bits(x.cpu()).reshape(-1, hidden), synth.bits(w_qkv.cpu())
+    wqb, wkb = synth.bits(w_q.cpu()), synth.bits(w_k.cpu())
+    cos, sin = oracle.rope_table_1d(P * S_l, D, theta=theta)
+    rng = np.random.default_rng(0)
+    n, reps, dt = 16, 0, 0.0
+    while dt < min_seconds:
+        rows = rng.integers(0, xb.shape[0], size=n)
+        pos = (rows // (B * S_l)) * S_l + rows % S_l
+        t0 = time.perf_counter()
+        oracle.qkv_proj_norm_rope_rows(xb[rows], "bf16", wb, H, H, D, wqb, wkb, eps, cos, sin, pos)
+        dt += time.perf_counter() - t0
+        reps += 1
+    flops = 2.0 * reps * n * wb.shape[0] * hidden
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": "%d batches of %d random token rows through the projection, QK-norm and RoPE "
+                      "(%d x %d weight) in %.1f s, single-threaded C oracle in double"
+                      % (reps, n, wb.shape[0], hidden, dt)}
+
+
 WORKLOADS = {"video_dit": setup_video_dit, "wan_long": setup_wan_long, "gqa": setup_gqa, "tiny": setup_tiny,
-             "spatial": setup_spatial}
+             "spatial": setup_spatial, "video_dit_proj": setup_video_dit_proj}
 
 
 def calibrate_copy(args, torch, UlyssesContext):
@@ -287,10 +370,13 @@ def main():
     w = setup["workload"]
     ctx = setup["ctx"]
     step, step_two_stream = setup["step"], setup.get("step_two_stream")
-    args.bytes_per_step = setup["bytes_per_step"]
+    step_per_operator = setup.get("step_per_operator")
+    args.bytes_per_step = setup["bytes_per_step"]        # the step's work: bytes, or flops for TFLOP/s
+    unit, unit_div = setup.get("unit", "GB/s"), setup.get("unit_div", 1e9)
+    name = setup.get("name", w.name)
     if step_two_stream is None:
         args.no_two_stream = True
-    print("bench: %s on %s, %d warmup + %d timed steps" % (w.name, torch.cuda.get_device_name(0),
+    print("bench: %s on %s, %d warmup + %d timed steps" % (name, torch.cuda.get_device_name(0),
                                                          args.warmup, args.steps), file=sys.stderr, flush=True)
 
     def timed(fn, steps):
@@ -305,8 +391,12 @@ def main():
         step()
         if not args.no_two_stream:
             step_two_stream()
+        if step_per_operator is not None:
+            step_per_operator()
     torch.cuda.synchronize()
-    dom_kind, dom_bytes, dom_name = setup["dominant"]
+    dom_kind, dom_bytes, dom_name = setup["dominant"][:3]
+    dom_bound, dom_peak, dom_unit = (setup["dominant"][3:] if len(setup["dominant"]) > 3
+                                     else ("hbm", HBM_PEAK_GBS, "GB/s"))
     if not args.no_profile:
         # time only the dominant kernel, one launch in PROFILE_EVERY: every event pair adds
         # latency between kernels
@@ -314,7 +404,7 @@ def main():
         ctx.profile_reset()
     wall = timed(step, args.steps)
     ms_per_step = wall * 1e3 / args.steps
-    value = args.bytes_per_step / (wall / args.steps) / 1e9
+    value = args.bytes_per_step / (wall / args.steps) / unit_div
 
     kernels = {}
     roofline = None
@@ -322,16 +412,20 @@ def main():
         ms, n = ctx.profile_read(dom_kind)
         if n:
             avg_us = ms * 1e3 / n
+            div = 1e9 if dom_unit == "GB/s" else 1e12
             kernels[dom_kind] = {"timed_launches": n, "launches": args.steps, "avg_us": round(avg_us, 2),
-                                 "bytes_per_launch": dom_bytes, "GB_s": round(dom_bytes / (avg_us * 1e-6) / 1e9, 1)}
+                                 "work_per_launch": dom_bytes,
+                                 dom_unit.replace("/", "_"): round(dom_bytes / (avg_us * 1e-6) / div, 1)}
         ctx.profile(False)
         ctx.profile_reset()
         dom = kernels.get(dom_kind)
         if dom:
-            achieved = dom["GB_s"]
-            roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(w.name),
-                        "kernel": dom_name, "algorithmic_bytes_per_launch": dom_bytes, "avg_us": dom["avg_us"]}
+            achieved = dom[dom_unit.replace("/", "_")]
+            roofline = {"bound": dom_bound, "achieved": achieved, "peak": dom_peak, "unit": dom_unit,
+                        "frac": round(achieved / dom_peak, 4),
+                        "traffic": traffic_from_profiles(name) if dom_bound == "hbm" else None,
+                        "kernel": dom_name, "avg_us": dom["avg_us"],
+                        ("algorithmic_bytes_per_launch" if dom_bound == "hbm" else "flops_per_launch"): dom_bytes}
 
     # the two-stream form of the same step, timed the same way (no events)
     two_stream = None
@@ -339,6 +433,14 @@ def main():
         wall2 = timed(step_two_stream, args.steps)
         two_stream = {"ms_per_step": round(wall2 * 1e3 / args.steps, 5),
                       "GB_s": round(args.bytes_per_step / (wall2 / args.steps) / 1e9, 2)}
+
+    per_operator = None
+    if step_per_operator is not None:
+        wall3 = timed(step_per_operator, args.steps)
+        per_operator = {"path": "torch linear (hipBLASLt) writing qkv, then fused_qk_norm_rope_scatter, wait, gather",
+                        "ms_per_step": round(wall3 * 1e3 / args.steps, 5),
+                        unit.replace("/", "_"): round(args.bytes_per_step / (wall3 / args.steps) / unit_div, 2),
+                        "fused_speedup": round(wall3 / wall, 4)}
 
     cold = None
     if args.cold:
@@ -354,7 +456,8 @@ def main():
             times.append(e0.elapsed_time(e1))
         times.sort()
         med = times[len(times) // 2]
-        cold = {"median_ms": round(med, 4), "GB_s": round(args.bytes_per_step / (med * 1e-3) / 1e9, 1),
+        cold = {"median_ms": round(med, 4),
+                unit.replace("/", "_"): round(args.bytes_per_step / (med * 1e-3) / unit_div, 1),
                 "p10_ms": round(times[2], 4), "p90_ms": round(times[17], 4)}
 
     ctx.close()
@@ -363,11 +466,15 @@ def main():
     if not args.no_cpu_baseline and "cpu_inputs" in setup:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         cpu = cpu_baseline(args, setup["cpu_inputs"])
+    elif not args.no_cpu_baseline and "cpu_proj" in setup:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_proj(args, setup["cpu_proj"])
 
     rec = {
-        "metric": METRIC if args.workload == "video_dit" else "Ulysses exchange GB/s, workload %s" % w.name,
+        "metric": (METRIC if args.workload == "video_dit"
+                   else setup.get("metric", "Ulysses exchange GB/s, workload %s" % name)),
         "value": round(value, 2),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -378,12 +485,15 @@ def main():
         "dtype": setup["dtype"],
         "data": setup["data"],
         "config": setup["config"],
-        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": roofline,
         "kernels": kernels,
         "two_stream": two_stream,
         "cpu_baseline": cpu,
     }
+    if unit == "GB/s":
+        rec["hbm_frac"] = round(value / HBM_PEAK_GBS, 4)
+    if per_operator:
+        rec["per_operator"] = per_operator
     if cold:
         rec["cold_cache"] = cold
     print(json.dumps(rec), flush=True)

@@ -35,7 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include "uly.h"
-#include "uly_internal.h"
+#include "uly_proj.h"
 
 namespace uly {
 namespace {
@@ -407,8 +407,9 @@ void proj_kernel(ProjArgs a) {
         const uint32_t kn = kt + kStages - 1, sn = (kt + kStages - 1) % kStages;
         if (!kSpread && more) issue(kn, sn, 0, 1);
         const uint4 *sa = lds + st * (kSlotsA + kSlotsB), *sb = sa + kSlotsA;
+        constexpr int KS = kProjTileK / 16;
 #pragma unroll
-        for (int ks = 0; ks < kProjTileK / 16; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             const int c = ks * 2 + fk;
             uint4 fa[4], fb[kTB];
 #pragma unroll
@@ -416,7 +417,7 @@ void proj_kernel(ProjArgs a) {
 #pragma unroll
             for (int tb = 0; tb < kTB; ++tb) fb[tb] = sb[swz(wt * kWaveT + tb * 32 + fr, c)];
             // the next stage's loads, spread over the K steps between the products
-            if (kSpread && more) issue(kn, sn, ks, kProjTileK / 16);
+            if (kSpread && more) issue(kn, sn, ks, KS);
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll

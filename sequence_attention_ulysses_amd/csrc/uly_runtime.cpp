@@ -24,6 +24,7 @@
 
 #include "uly.h"
 #include "uly_internal.h"
+#include "uly_proj.h"
 
 using namespace uly;
 
