@@ -105,7 +105,8 @@ struct RowMapArgs {
 
 // Launch wrappers (uly_kernels.hip).  They only enqueue; the caller checks
 // hipGetLastError().
-void launch_relayout(const CopyBatch &b, hipStream_t stream);
+// system_scope: the cache-resident gather policy (kGather*), else kScatter*.
+void launch_relayout(const CopyBatch &b, bool system_scope, hipStream_t stream);
 void launch_norm_rope(const NormRopeArgs &a, int lanes, int dtype, bool uniform, bool tile, uint32_t blocks,
                       hipStream_t stream);
 void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
@@ -131,17 +132,37 @@ void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
 #ifndef ULY_RELAYOUT_NT_STORE
 #define ULY_RELAYOUT_NT_STORE 1
 #endif
+#ifndef ULY_SCATTER_LOAD
+#define ULY_SCATTER_LOAD 1
+#endif
+#ifndef ULY_SCATTER_STORE
+#define ULY_SCATTER_STORE 1
+#endif
+#ifndef ULY_GATHER_LOAD
+#define ULY_GATHER_LOAD 2
+#endif
+#ifndef ULY_GATHER_STORE
+#define ULY_GATHER_STORE 2
+#endif
 #ifndef ULY_ROPE_NT_LOAD
 #define ULY_ROPE_NT_LOAD 1
 #endif
 #ifndef ULY_ROPE_NT_STORE
 #define ULY_ROPE_NT_STORE 1
 #endif
-// Non-temporal (streaming) policy of the operand loads and stores per kernel.
-constexpr bool kRelayoutNtLoad = ULY_RELAYOUT_NT_LOAD;
-constexpr bool kRelayoutNtStore = ULY_RELAYOUT_NT_STORE;
-constexpr bool kRopeNtLoad = ULY_ROPE_NT_LOAD;
-constexpr bool kRopeNtStore = ULY_ROPE_NT_STORE;
+// Cache policy of the operand loads and stores per kernel: 0 ordinary,
+// 1 non-temporal (streaming), 2 system scope.
+constexpr int kRelayoutNtLoad = ULY_RELAYOUT_NT_LOAD;     // row maps (pad/trim, spatial)
+constexpr int kRelayoutNtStore = ULY_RELAYOUT_NT_STORE;
+constexpr int kScatterLoad = ULY_SCATTER_LOAD;             // Q/K/V scatter, chunk exchange
+constexpr int kScatterStore = ULY_SCATTER_STORE;
+constexpr int kGatherLoad = ULY_GATHER_LOAD;               // output gather within the Infinity Cache
+constexpr int kGatherStore = ULY_GATHER_STORE;
+// A gather whose input + output bytes fit in the 256 MB Infinity Cache uses
+// the system-scope policy; larger gathers stream with the scatter policy.
+constexpr int64_t kCacheResidentBytes = int64_t(256) << 20;
+constexpr int kRopeNtLoad = ULY_ROPE_NT_LOAD;
+constexpr int kRopeNtStore = ULY_ROPE_NT_STORE;
 constexpr int kThreads = ULY_THREADS;
 constexpr int kCopyUnroll = ULY_COPY_UNROLL;             // 16-byte vectors per thread
 constexpr uint32_t kCopyVecsPerBlock = kThreads * kCopyUnroll;

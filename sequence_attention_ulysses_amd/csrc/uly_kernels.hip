@@ -30,23 +30,34 @@ typedef __attribute__((address_space(1))) u32x4 global_u32x4;
 
 // All operands live in device (global) memory: the explicit address space
 // keeps the accesses global_load/store instead of flat ones.  Operand data
-// streams through exactly once, so by default its 16-byte accesses are
-// non-temporal (they do not displace lines that are reused); each kernel
-// picks the policy of its loads and of its stores (uly_internal.h).
-template <bool NT>
+// streams through exactly once; each kernel picks the cache policy of its
+// loads and of its stores (uly_internal.h).  Measured on the video-DiT step:
+// a gather whose input and output fit in the 256 MB Infinity Cache runs
+// fastest with system-scope accesses (sc0 sc1, through a volatile access:
+// video-DiT output gather 35.8 -> 31.0 us), larger gathers and the scatters
+// with non-temporal ones (system scope there: GQA Q/K/V scatter 527 -> 553
+// us, GQA and Wan gathers 2 % slower),
+// and the fused norm + RoPE kernel with non-temporal ones too (system scope:
+// 107 -> 133 us, since a volatile access is followed by a wait and the
+// kernel keeps four loads per thread in flight).
+// Policy 0: ordinary access; 1: non-temporal (nt); 2: system scope (sc0 sc1,
+// through a volatile access).
+template <int POL>
 __device__ __forceinline__ uint4 load16(const void *p) {
     const global_u32x4 *g = (const global_u32x4 *)p;
     u32x4 v;
-    if constexpr (NT) v = __builtin_nontemporal_load(g);
+    if constexpr (POL == 1) v = __builtin_nontemporal_load(g);
+    else if constexpr (POL == 2) v = *(const volatile global_u32x4 *)g;
     else v = *g;
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <bool NT>
+template <int POL>
 __device__ __forceinline__ void store16(void *p, uint4 v) {
     global_u32x4 *g = (global_u32x4 *)p;
     const u32x4 w = {v.x, v.y, v.z, v.w};
-    if constexpr (NT) __builtin_nontemporal_store(w, g);
+    if constexpr (POL == 1) __builtin_nontemporal_store(w, g);
+    else if constexpr (POL == 2) *(volatile global_u32x4 *)g = w;
     else *g = w;
 }
 
@@ -84,6 +95,7 @@ __device__ __forceinline__ uint32_t logical_block(uint32_t bid, uint32_t grid) {
 // [p[i].first_block, p[i+1].first_block) belong to operand i, so the three
 // copies fill the machine together instead of draining one after another.
 // ---------------------------------------------------------------------------
+template <int LP, int SP>
 __global__ __launch_bounds__(kThreads) void relayout_kernel(CopyBatch b) {
     const uint32_t bid = logical_block(blockIdx.x, gridDim.x);
     int pi = 0;
@@ -107,13 +119,13 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(CopyBatch b) {
                                int64_t(i2) * P.ss[2] + int64_t(i3) * P.ss[3] + uint64_t(c) * 16u;
             d[u] = P.dst + int64_t(i0) * P.ds[0] + int64_t(i1) * P.ds[1] + int64_t(i2) * P.ds[2] +
                    int64_t(i3) * P.ds[3] + uint64_t(c) * 16u;
-            v[u] = load16<kRelayoutNtLoad>(s);
+            v[u] = load16<LP>(s);
         }
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
         const uint32_t i = first + u * kThreads;
-        if (i < P.total) store16<kRelayoutNtStore>(d[u], v[u]);
+        if (i < P.total) store16<SP>(d[u], v[u]);
     }
 }
 
@@ -416,8 +428,12 @@ __global__ __launch_bounds__(kThreads) void rowmap_kernel(RowMapArgs a) {
 
 }  // namespace
 
-void launch_relayout(const CopyBatch &b, hipStream_t stream) {
-    hipLaunchKernelGGL(relayout_kernel, dim3(b.blocks), dim3(kThreads), 0, stream, b);
+void launch_relayout(const CopyBatch &b, bool system_scope, hipStream_t stream) {
+    if (system_scope)
+        hipLaunchKernelGGL((relayout_kernel<kGatherLoad, kGatherStore>), dim3(b.blocks), dim3(kThreads), 0, stream, b);
+    else
+        hipLaunchKernelGGL((relayout_kernel<kScatterLoad, kScatterStore>), dim3(b.blocks), dim3(kThreads), 0, stream,
+                           b);
 }
 
 template <int L, int T>

@@ -621,7 +621,7 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
         if (cerr != hipSuccess) return poison(c, cerr, "hipMemcpy2DAsync");
         return mark_pending(c, c->comm);
     }
-    if ((st = launch(c, ULY_K_SCATTER, c->comm, [&] { launch_relayout(batch, c->comm); })) != ULY_OK)
+    if ((st = launch(c, ULY_K_SCATTER, c->comm, [&] { launch_relayout(batch, false, c->comm); })) != ULY_OK)
         return st;
     return mark_pending(c, c->comm);
 }
@@ -904,7 +904,8 @@ uly_status ulysses_gather_out(uly_ctx *c, const uly_tensor *o, const char *tag, 
     if (batch.n == 0) return ULY_OK;
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
-    return launch(c, ULY_K_GATHER, caller, [&] { launch_relayout(batch, caller); });
+    const bool resident = 2 * int64_t(batch.p[0].total) * 16 <= kCacheResidentBytes;
+    return launch(c, ULY_K_GATHER, caller, [&] { launch_relayout(batch, resident, caller); });
 }
 
 uly_status uly_exchange_chunks(uly_ctx *c, const void *x, void *y, int64_t chunk_bytes, hipStream_t stream) {
@@ -931,7 +932,7 @@ uly_status uly_exchange_chunks(uly_ctx *c, const void *x, void *y, int64_t chunk
     if (batch.n == 0) return ULY_OK;
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
-    return launch(c, ULY_K_SCATTER, stream, [&] { launch_relayout(batch, stream); });
+    return launch(c, ULY_K_SCATTER, stream, [&] { launch_relayout(batch, false, stream); });
 }
 
 // ---- sequence padding ------------------------------------------------------
