@@ -212,20 +212,21 @@ __device__ __forceinline__ T sel3(uint32_t i, T a, T b, T c) {
 #endif
 
 // One head slot of a lane group: where its rows come from and go to.
-template <int DT>
 struct Slot {
     const uint16_t *src;   // this lane's 8 elements of the head, token offsets still to add
     uint16_t *dst;
+    const uint16_t *w;     // this lane's 8 norm weights (V: any readable 16 bytes, unused)
     int64_t s_rank, s_b, s_s, d_b, d_g;
-    float w[8];
     bool rope;             // Q or K (normalised and rotated); V is copied
     bool live;             // the slot exists (the last slots of a group may not)
 };
 
-template <int DT, bool UNI>
-__device__ __forceinline__ Slot<DT> make_slot(const NormRopeArgs &a, uint32_t hh, uint32_t R, uint32_t lane) {
+// Addresses only: the loads are issued by the caller, rows first, so that
+// no load result is consumed before every load of the trip is in flight.
+template <bool UNI>
+__device__ __forceinline__ Slot make_slot(const NormRopeArgs &a, uint32_t hh, uint32_t R, uint32_t lane) {
     const NormRopeOperand &o0 = a.op[0], &o1 = a.op[1], &o2 = a.op[2];
-    Slot<DT> sl;
+    Slot sl;
     sl.live = hh < R;
     const uint32_t hc = sl.live ? hh : R - 1;                  // dead slots read a valid row
     const uint32_t hh_op = UNI ? __builtin_amdgcn_readfirstlane(hc) : hc;
@@ -243,10 +244,8 @@ __device__ __forceinline__ Slot<DT> make_slot(const NormRopeArgs &a, uint32_t hh
     sl.src = sel3(oi, o0.src, o1.src, o2.src) + int64_t(h) * sel3(oi, o0.s_h, o1.s_h, o2.s_h) + lane * 8;
     sl.dst = sel3(oi, o0.dst, o1.dst, o2.dst) + int64_t(qd) * sel3(oi, o0.d_q, o1.d_q, o2.d_q) +
              int64_t(j) * sel3(oi, o0.d_j, o1.d_j, o2.d_j) + lane * 8;
+    sl.w = sel3(oi, o0.w, o1.w, o2.w) + lane * 8;
     sl.rope = oi < 2;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sl.w[i] = 0.f;
-    if (sl.rope) unpack8<DT>(load16_cached(sel3(oi, o0.w, o1.w, o2.w) + lane * 8), sl.w);
     return sl;
 }
 
@@ -300,31 +299,34 @@ __global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_ker
             a.bdiv.divmod(rb, tr[t], tb[t]);
         }
         g = tr[t] * a.S_l + ts[t];
-        cs[t] = make_float4(1.f, 1.f, 1.f, 1.f);
-        sn[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (a.H01 > 0) {
-            const size_t t_off = size_t(g) * half + lane * 4;
-            cs[t] = load_table4(a.cos_tab + t_off);
-            sn[t] = load_table4(a.sin_tab + t_off);
-        }
+        // unconditional: the table covers every position (a V-only call reads
+        // and ignores it), and a load under a branch would be waited for at once
+        const size_t t_off = size_t(g) * half + lane * 4;
+        cs[t] = load_table4(a.cos_tab + t_off);
+        sn[t] = load_table4(a.sin_tab + t_off);
     }
 
     // Every lane of a group runs the same slot and token trips; dead slots
     // and tokens past the end are computed on a valid row and not stored, so
     // every lane of a group takes part in every DPP exchange.
     for (uint32_t hh = grp; hh < R; hh += GROUPS * SU) {
-        Slot<DT> sl[SU];
-        uint4 raw[SU][TU];
+        Slot sl[SU];
+        uint4 raw[SU][TU], wraw[SU];
 #pragma unroll
-        for (int u = 0; u < SU; ++u) {
-            sl[u] = make_slot<DT, UNI>(a, hh + u * GROUPS, R, lane);
+        for (int u = 0; u < SU; ++u) sl[u] = make_slot<UNI>(a, hh + u * GROUPS, R, lane);
+        // every row load of the trip first, then the (cache-resident) weights
+#pragma unroll
+        for (int u = 0; u < SU; ++u)
 #pragma unroll
             for (int t = 0; t < TU; ++t)
                 raw[u][t] = load16<kRopeNtLoad>(sl[u].src + (int64_t(tr[t]) * sl[u].s_rank + int64_t(tb[t]) * sl[u].s_b +
                                                 int64_t(ts[t]) * sl[u].s_s));
-        }
+#pragma unroll
+        for (int u = 0; u < SU; ++u) wraw[u] = load16_cached(sl[u].w);
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
+            float w[8];
+            unpack8<DT>(wraw[u], w);
 #pragma unroll
             for (int t = 0; t < TU; ++t) {
                 float x[8];
@@ -340,8 +342,8 @@ __global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_ker
                 uint32_t out[4];
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const float n0 = x[2 * p] * inv * sl[u].w[2 * p];
-                    const float n1 = x[2 * p + 1] * inv * sl[u].w[2 * p + 1];
+                    const float n0 = x[2 * p] * inv * w[2 * p];
+                    const float n1 = x[2 * p + 1] * inv * w[2 * p + 1];
                     const float y0 = n0 * c[p] - n1 * sv[p];
                     const float y1 = n0 * sv[p] + n1 * c[p];
                     out[p] = pack2<DT>(y0, y1);

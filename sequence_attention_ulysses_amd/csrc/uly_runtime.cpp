@@ -228,6 +228,11 @@ uly_status resolve_target(uly_ctx *c, const char *name, const char *tag, void *e
     return ULY_OK;
 }
 
+// Timing events only measure: they need no system-scope fence (an L2
+// write-back and invalidate each time one is recorded, which would both
+// lengthen the bracketed interval and slow the launches after it).
+constexpr unsigned kTimingEventFlags = hipEventDisableSystemFence;
+
 hipEvent_t take_event(std::vector<hipEvent_t> &pool, unsigned flags, hipError_t &err) {
     if (!pool.empty()) {
         hipEvent_t e = pool.back();
@@ -267,9 +272,9 @@ uly_status launch(uly_ctx *c, int kind, hipStream_t s, F &&enqueue) {
     hipError_t err = hipSuccess;
     const bool timed = ((c->profile_mask >> kind) & 1) && (c->profile_seen[kind]++ % c->profile_every == 0);
     if (timed) {
-        e0 = take_event(c->timing_pool, hipEventDefault, err);
+        e0 = take_event(c->timing_pool, kTimingEventFlags, err);
         if (!e0) return poison(c, err, "hipEventCreate");
-        e1 = take_event(c->timing_pool, hipEventDefault, err);
+        e1 = take_event(c->timing_pool, kTimingEventFlags, err);
         if (!e1) return poison(c, err, "hipEventCreate");
         if ((err = hipEventRecord(e0, s)) != hipSuccess) return poison(c, err, "hipEventRecord");
     }
@@ -705,7 +710,10 @@ static uly_status fused_scatter(uly_ctx *c, const uly_tensor *q, const uly_tenso
         const int64_t Hl = x.H / c->P, Sg = x.S * c->P;
         o.src = reinterpret_cast<const uint16_t *>(x.data);
         o.dst = reinterpret_cast<uint16_t *>(dsts[i]);
-        o.w = static_cast<const uint16_t *>(wts[i]);
+        // V rows are copied, but the kernel reads a weight row for every slot
+        // without a branch: point V's at the table, which holds at least 2*D
+        // readable bytes.
+        o.w = static_cast<const uint16_t *>(wts[i] ? wts[i] : static_cast<const void *>(cos_tab));
         o.s_rank = x.rank_stride;
         o.s_b = x.sb;
         o.s_s = x.ss;
