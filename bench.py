@@ -60,6 +60,21 @@ def traffic_from_profiles(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_cpu() -> str:
+    """The host CPU's model name and the logical CPUs this process may use."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return "%s, %d logical CPUs available" % (model, n)
+
+
 def cpu_baseline(args, inputs, min_seconds: float = 10.0):
     """The CPU oracle, as it stands, on whole steps of the same workload,
     repeated until about `min_seconds` of CPU work."""
@@ -85,8 +100,8 @@ def cpu_baseline(args, inputs, min_seconds: float = 10.0):
     return {"value": round(steps * args.bytes_per_step / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": "%d full steps of the workload (V scatter, Q/K norm+RoPE scatter, output gather; "
-                      "%d algorithmic bytes each) in %.1f s, single-threaded C oracle in double"
-                      % (steps, args.bytes_per_step, dt)}
+                      "%d algorithmic bytes each) in %.1f s, single-threaded C oracle in double; host: %s"
+                      % (steps, args.bytes_per_step, dt, host_cpu())}
 
 
 # ---------------------------------------------------------------------------
@@ -95,13 +110,13 @@ def cpu_baseline(args, inputs, min_seconds: float = 10.0):
 # element read once, each output element written once, real tokens only),
 # the dominant kernel (kind, bytes per launch, name) and the JSON config.
 # ---------------------------------------------------------------------------
-def setup_video_dit(torch, dev, synth, rope_table_1d, UlyssesContext):
+def setup_video_dit(torch, dev, synth, rope_table_1d, UlyssesContext, dtype="bf16"):
     w = synth.VIDEO_DIT
     P, B, S_l, H, D = w.P, w.B, w.S_l, w.Hq, w.D
     n_tensor = P * B * S_l * H * D * 2
-    qkv = synth.normal((P, B, S_l, 3, H, D), "bf16", 0)
-    w_q, w_k = synth.norm_weight(D, "bf16", 1), synth.norm_weight(D, "bf16", 2)
-    o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 3)
+    qkv = synth.normal((P, B, S_l, 3, H, D), dtype, 0)
+    w_q, w_k = synth.norm_weight(D, dtype, 1), synth.norm_weight(D, dtype, 2)
+    o = synth.normal((P, B, P * S_l, H // P, D), dtype, 3)
     cos, sin = rope_table_1d(P * S_l, D, theta=w.theta)
     g_qkv, g_wq, g_wk, g_o = qkv.to(dev), w_q.to(dev), w_k.to(dev), o.to(dev)
     g_cos, g_sin = cos.to(dev), sin.to(dev)
@@ -123,7 +138,7 @@ def setup_video_dit(torch, dev, synth, rope_table_1d, UlyssesContext):
             "bytes_per_step": 3 * 2 * n_tensor + 2 * n_tensor,
             "dominant": ("norm_rope", 6 * n_tensor,
                          "norm_rope_kernel<16,bf16> (Q/K RMSNorm+RoPE scatter with V in the same grid)"),
-            "cpu_inputs": (qkv, w_q, w_k, o), "dtype": "bf16",
+            "cpu_inputs": (qkv, w_q, w_k, o), "dtype": dtype,
             "data": "synthetic N(0,1) activations, N(1,0.1) norm weights, 1-D RoPE theta 1e4 (seeded)",
             "config": {"workload": w.name, "P": P, "B": B, "S_local": S_l, "S": P * S_l, "H": H, "D": D,
                        "v_source": "strided from fused QKV [B,S_local,3,H,D]", "parallelism": "ulysses-p4-emulated",
@@ -309,12 +324,52 @@ def cpu_baseline_proj(args, proj_inputs, min_seconds: float = 10.0):
     flops = 2.0 * reps * n * wb.shape[0] * hidden
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "sample": "%d batches of %d random token rows through the projection, QK-norm and RoPE "
-                      "(%d x %d weight) in %.1f s, single-threaded C oracle in double"
-                      % (reps, n, wb.shape[0], hidden, dt)}
+                      "(%d x %d weight) in %.1f s, single-threaded C oracle in double; host: %s"
+                      % (reps, n, wb.shape[0], hidden, dt, host_cpu())}
 
 
 WORKLOADS = {"video_dit": setup_video_dit, "wan_long": setup_wan_long, "gqa": setup_gqa, "tiny": setup_tiny,
              "spatial": setup_spatial, "video_dit_proj": setup_video_dit_proj}
+
+
+def measure_protocol(args, torch, dev, setup, step, timed, samples: int = 100):
+    """The rest of the timing protocol, outside the timed region: the spread
+    of single steps (events on the stream every kernel of the step runs on),
+    an A/A repeat of the timed loop, a plain device copy of the step's bytes,
+    and the same step in fp16 (a relayout moves bytes, so the rate must not
+    depend on the 16-bit type)."""
+    from sequence_attention_ulysses_amd import UlyssesContext, rope_table_1d, synth
+
+    nbytes = setup["bytes_per_step"]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    for e0, e1 in ev:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    pick = lambda q: t[min(len(t) - 1, int(q * len(t)))]
+    spread = {"samples": samples, "median_us": round(pick(0.5) * 1e3, 2), "p10_us": round(pick(0.1) * 1e3, 2),
+              "p90_us": round(pick(0.9) * 1e3, 2), "GB_s_at_median": round(nbytes / (pick(0.5) * 1e-3) / 1e9, 1)}
+
+    wall = timed(step, args.steps)
+    aa = {"ms_per_step": round(wall * 1e3 / args.steps, 5), "GB_s": round(nbytes / (wall / args.steps) / 1e9, 2)}
+
+    # a device-to-device copy moving the same bytes (half read, half written)
+    src = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    wall = timed(lambda: dst.copy_(src), args.steps)
+    copy = {"bytes_copied": nbytes // 2, "ms": round(wall * 1e3 / args.steps, 5),
+            "GB_s": round(nbytes / (wall / args.steps) / 1e9, 2)}
+    del src, dst
+
+    f16 = setup_video_dit(torch, dev, synth, rope_table_1d, UlyssesContext, dtype="f16")
+    for _ in range(args.warmup):
+        f16["step"]()
+    wall = timed(f16["step"], args.steps)
+    f16["ctx"].close()
+    fp16 = {"ms_per_step": round(wall * 1e3 / args.steps, 5), "GB_s": round(nbytes / (wall / args.steps) / 1e9, 2)}
+    return {"step_spread": spread, "aa_repeat": aa, "device_copy_control": copy, "fp16_same_shape": fp16}
 
 
 def calibrate_copy(args, torch, UlyssesContext):
@@ -460,6 +515,8 @@ def main():
                 unit.replace("/", "_"): round(args.bytes_per_step / (med * 1e-3) / unit_div, 1),
                 "p10_ms": round(times[2], 4), "p90_ms": round(times[17], 4)}
 
+    extra = measure_protocol(args, torch, dev, setup, step, timed) if args.workload == "video_dit" else None
+
     ctx.close()
 
     cpu = None
@@ -496,6 +553,8 @@ def main():
         rec["per_operator"] = per_operator
     if cold:
         rec["cold_cache"] = cold
+    if extra:
+        rec.update(extra)
     print(json.dumps(rec), flush=True)
 
 
