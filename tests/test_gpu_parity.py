@@ -231,6 +231,20 @@ def test_fused_single_operand_and_determinism(dev, orc):
                        "bf16", "k")
 
 
+def test_fused_v_only_is_a_plain_scatter(dev, orc):
+    """A fused call with V alone (no row is normalised) still reads a table row and a
+    weight row per slot without a branch; its output is the bit-exact scatter."""
+    P, B, S_l, H, D = 4, 2, 40, 8, 128
+    v = synth.normal((P, B, S_l, H, D), "bf16", 12, dev)
+    cos, sin = rope_table_1d(P * S_l, D)
+    with UlyssesContext(P, device=0) as ctx:
+        _, _, yv = ctx.fused_qk_norm_rope_scatter(None, None, None, None, cos.to(dev), sin.to(dev), v=v,
+                                                  tags=(None, None, "v_only"))
+        ctx.wait()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_bits(yv), orc.scatter(to_bits(v)))
+
+
 def test_fused_edge_rows(dev, orc):
     """Zero rows (padding) give exactly +-0; constant rows hit the closed form."""
     P, B, S_l, H, D = 2, 1, 16, 4, 128
