@@ -729,10 +729,10 @@ static uly_status fused_scatter(uly_ctx *c, const uly_tensor *q, const uly_tenso
     }
     const uint32_t Hsum = Hrows[0] + Hrows[1] + Hrows[2];
     const int64_t tokens = int64_t(c->P) * B * S;
-    if (c->host_only) return host_only_launch(c);
-    if (tokens == 0) return ULY_OK;
     if (tokens * Hsum >= kMaxVecs || tokens >= kMaxVecs)
         return fail(ULY_E_UNSUPPORTED, "too many rows for one launch (%lld)", (long long)(tokens * Hsum));
+    if (c->host_only) return host_only_launch(c);
+    if (tokens == 0) return ULY_OK;
     a.cos_tab = cos_tab;
     a.sin_tab = sin_tab;
     a.rpt = FastDiv::make(Hsum);

@@ -300,6 +300,48 @@ def _check_fused_rows(orc, x_bits, y_dev, dtype, w_bits, cos, sin, windows, what
             assert_close16(sub, want, dtype, "%s r=%d s=[%d,%d)" % (what, r, s0, s1))
 
 
+def test_offsets_beyond_4gib(dev, orc):
+    """Rank slabs and targets larger than 4 GiB (P=2, S_l=2^19+32, H=32, D=128 bf16:
+    4 GiB per slab, 8 GiB per tensor), so every byte offset past 2^32 must be formed in
+    64 bits: the plain scatter, the fused Q/K/V launch and the gather, checked against
+    the oracle on token windows at the start, middle and end of each slab, and the
+    gather of the scattered V against V itself in full."""
+    P, B, S_l, H, D = 2, 1, (1 << 19) + 32, 32, 128
+    n = P * B * S_l * H * D * 2
+    assert n // P > 1 << 32
+    free, _ = torch.cuda.mem_get_info()
+    if free < 10 * n:
+        pytest.skip("needs %.0f GiB of free device memory" % (10 * n / 2 ** 30))
+    print("beyond-4GiB case: P=%d S_l=%d H=%d D=%d bf16, %.1f GiB per tensor" % (P, S_l, H, D, n / 2 ** 30), flush=True)
+    q, k, v = contiguous_qkv(P, B, S_l, H, D, "bf16", 4000, dev)
+    w_q, w_k = synth.norm_weight(D, "bf16", 4003, dev), synth.norm_weight(D, "bf16", 4004, dev)
+    cos, sin = rope_table_1d(P * S_l, D)
+    ocos, osin = orc.rope_table_1d(P * S_l, D)
+    win = [(0, 32), (S_l // 2 - 16, S_l // 2 + 16), (S_l - 32, S_l)]
+    with UlyssesContext(P, device=0) as ctx:
+        _, _, yv = ctx.scatter_qkv(v=v, tags=(None, None, "v_plain"))
+        yq, yk, yv2 = ctx.fused_qk_norm_rope_scatter(q, k, w_q, w_k, cos.to(dev), sin.to(dev), v=v)
+        ctx.wait()
+        z = ctx.gather_out(yv, tag="out")
+        torch.cuda.synchronize()
+        assert torch.equal(z.view(torch.int16), v.view(torch.int16))
+        assert torch.equal(yv2.view(torch.int16), yv.view(torch.int16))
+        for s0, s1 in win:
+            rows = torch.cat([torch.arange(r * S_l + s0, r * S_l + s1) for r in range(P)]).to(dev)
+            np.testing.assert_array_equal(to_bits(yv.index_select(2, rows)), orc.scatter(to_bits(v[:, :, s0:s1])))
+        for x, w, y, name in ((q, w_q, yq, "q"), (k, w_k, yk, "k")):
+            for s0, s1 in win:
+                xs = orc.widen(to_bits(x[:, :, s0:s1]), "bf16")
+                pos = np.broadcast_to(np.arange(P)[:, None, None, None] * S_l + np.arange(s0, s1)[None, None, :, None],
+                                      (P, B, s1 - s0, H)).reshape(-1)
+                yo = orc.norm_rope_rows(xs.reshape(-1, D), orc.widen(to_bits(w), "bf16"), 1e-6, ocos, osin, pos)
+                yo = yo.reshape(P, B, s1 - s0, H, D)
+                for r in range(P):
+                    sub = y.index_select(2, torch.arange(r * S_l + s0, r * S_l + s1, device=dev))
+                    want = yo[r].reshape(B, s1 - s0, P, H // P, D).transpose(2, 0, 1, 3, 4)
+                    assert_close16(sub, want, "bf16", "%s r=%d s=[%d,%d)" % (name, r, s0, s1))
+
+
 def test_video_dit_block_full(dev, orc):
     """P=4, S_l=4096, H=24, D=128 bf16; V strided from fused QKV on the comm stream,
     fused Q/K norm + RoPE on the caller stream, grouped wait, output gather."""

@@ -252,6 +252,28 @@ def test_fused_rejections(lib, ctx4):
     assert _fused(lib, ctx4, q, k2, v=v_over) == _lib.E_OVERLAP
 
 
+def test_launch_size_limits(lib, ctx4):
+    """Flat 32-bit indices cover 2^31 16-byte vectors (32 GiB) per operand plan, and
+    2^31 rows per fused launch: larger calls are refused before anything is enqueued."""
+    GiB = 1 << 30
+    # per rank [1, 2^21, 32, 128] bf16 = 16 GiB; 4 ranks = 64 GiB = 2^32 vectors: too large
+    big = T(BASE, (1, 1 << 21, 32, 128))
+    assert scatter(lib, ctx4, q=big, tags=(None, None, None), outs=(BASE + 256 * GiB, None, None)) == _lib.E_UNSUPPORTED
+    assert b"too large" in lib.uly_last_error()
+    # just under the limit: [1, 2^19, 32, 128] per rank, 2^30 vectors in all: accepted (would launch)
+    ok = T(BASE, (1, 1 << 19, 32, 128))
+    assert scatter(lib, ctx4, q=ok, tags=(None, None, None), outs=(BASE + 256 * GiB, None, None)) == _lib.E_UNSUPPORTED
+    assert b"host-only" in lib.uly_last_error()
+    # the inverse: head-sharded [1, 2^23, 8, 128] per rank is 2^32 vectors in all
+    o = T(BASE, (1, 1 << 23, 8, 128))
+    assert lib.ulysses_gather_out(ctx4.h, ctypes.byref(o), None, BASE + 256 * GiB, None) == _lib.E_UNSUPPORTED
+    assert b"too large" in lib.uly_last_error()
+    # fused: 4 * 2^24 tokens x 64 rows = 2^32 rows in one launch
+    qf, kf = T(BASE, (1, 1 << 24, 32, 32)), T(BASE + 512 * GiB, (1, 1 << 24, 32, 32))
+    assert _fused(lib, ctx4, qf, kf, rows=4 << 24, outs=(BASE + 1024 * GiB, BASE + 2048 * GiB)) == _lib.E_UNSUPPORTED
+    assert b"too many rows" in lib.uly_last_error()
+
+
 def test_fail_stop_after_launch_failure(lib):
     c = Ctx(lib, 2)
     try:
