@@ -513,6 +513,7 @@ uly_status uly_target_register(uly_ctx *c, const char *tag, int mode, int dtype,
     int64_t elems = c->P;
     for (int i = 0; i < 4; ++i) {
         if (shape[i] < 1) return fail(ULY_E_INVAL, "target extents must be positive");
+        if (elems > (int64_t(1) << 56) / shape[i]) return fail(ULY_E_INVAL, "target extents overflow");
         elems *= shape[i];
     }
     if (!storage || !aligned16(storage)) return fail(ULY_E_INVAL, "storage null or not 16-byte aligned");
