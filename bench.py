@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Ulysses QKV scatter+gather GB/s and % HBM peak, P=4 bf16, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
-PROFILE_EVERY = 8
+PROFILE_EVERY = 16
 KERNEL_SOURCES = [os.path.join(ROOT, "sequence_attention_ulysses_amd", "csrc", f)
                   for f in ("uly_kernels.hip", "uly_internal.h", "fastdiv.h")]
 
@@ -418,7 +418,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="video_dit", choices=sorted(WORKLOADS),
                     help="video_dit (the headline, default) or another workload recorded for reference")
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
