@@ -121,10 +121,10 @@ void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
 #define ULY_ROPE_TOKENS 2
 #endif
 #ifndef ULY_ROPE_SLOTS
-#define ULY_ROPE_SLOTS 2
+#define ULY_ROPE_SLOTS 1
 #endif
 #ifndef ULY_ROPE_THREADS
-#define ULY_ROPE_THREADS 512
+#define ULY_ROPE_THREADS 768
 #endif
 #ifndef ULY_RELAYOUT_NT_LOAD
 #define ULY_RELAYOUT_NT_LOAD 1
