@@ -27,7 +27,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "uly_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ULY_ORACLE_LIB points the oracle at another build of uly_oracle.c (the
+# mutation tests load deliberately broken copies to show the pins catch them).
+_LIB = os.environ.get("ULY_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _lib = None
 
