@@ -426,6 +426,9 @@ def main():
     ap.add_argument("--no-profile", action="store_true", help="do not bracket launches with timing events")
     ap.add_argument("--no-two-stream", action="store_true",
                     help="skip the two-stream comparison (profiling runs then hold only the headline step)")
+    ap.add_argument("--route", choices=("kernel", "copy_engine", "caller"), default=None,
+                    help="how the plain Q/K/V scatter moves its operands (the library default: kernel on the "
+                         "comm stream); the workloads that use it are gqa and tiny")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", default=0,
                     help="instead of the step, run a plain device copy of MIB MiB (the library's relayout with "
                          "one rank) to calibrate HBM byte counters against a known size")
@@ -448,6 +451,9 @@ def main():
     setup = WORKLOADS[args.workload](torch, dev, synth, rope_table_1d, UlyssesContext)
     w = setup["workload"]
     ctx = setup["ctx"]
+    if args.route:
+        ctx.set_route(args.route)
+        setup["config"]["scatter_route"] = args.route
     step, step_two_stream = setup["step"], setup.get("step_two_stream")
     step_per_operator = setup.get("step_per_operator")
     args.bytes_per_step = setup["bytes_per_step"]        # the step's work: bytes, or flops for TFLOP/s

@@ -345,13 +345,17 @@ uly_status uly_get_stats(uly_ctx *ctx, uly_stats *out);
 uly_status uly_comm_stream(uly_ctx *ctx, hipStream_t *out);
 
 /* How ulysses_scatter_qkv moves its operands.  ULY_ROUTE_KERNEL (default):
- * one relayout kernel on the compute units.  ULY_ROUTE_COPY_ENGINE: one
- * 2-D copy per (source rank, destination rank, batch) block on the copy
- * engines, straight into the final layout, leaving the compute units to the
- * fused Q/K kernel ([P27 "Description": copy-engine transfers overlapping
- * Q/K preprocessing]).  Head bands of more than one head must be packed
- * (stride[2] == D), as for the kernel route. */
-typedef enum { ULY_ROUTE_KERNEL = 0, ULY_ROUTE_COPY_ENGINE = 1 } uly_route;
+ * one relayout kernel on the compute units, on the context's comm stream.
+ * ULY_ROUTE_COPY_ENGINE: one 2-D copy per (source rank, destination rank,
+ * batch) block on the copy engines, straight into the final layout, leaving
+ * the compute units to the fused Q/K kernel ([P27 "Description": copy-engine
+ * transfers overlapping Q/K preprocessing]).  ULY_ROUTE_CALLER: the same
+ * relayout kernel on the caller's stream itself, with no second stream and
+ * no fork or join events, for callers that do not overlap the scatter with
+ * other work (the copy is then ordered like any kernel on `caller`, and
+ * uly_wait has nothing to do for it on that stream).  Head bands of more
+ * than one head must be packed (stride[2] == D), as for the kernel route. */
+typedef enum { ULY_ROUTE_KERNEL = 0, ULY_ROUTE_COPY_ENGINE = 1, ULY_ROUTE_CALLER = 2 } uly_route;
 uly_status uly_set_route(uly_ctx *ctx, int route);
 
 /* Fault injection for tests of the fail-stop rule: the `after`-th next

@@ -34,6 +34,7 @@ MODE_SCATTER = 0
 MODE_GATHER = 1
 ROUTE_KERNEL = 0
 ROUTE_COPY_ENGINE = 1
+ROUTE_CALLER = 2
 
 K_SCATTER, K_NORM_ROPE, K_GATHER, K_PAD, K_SPATIAL, K_PROJ = range(6)
 KERNEL_KINDS = {"scatter": K_SCATTER, "norm_rope": K_NORM_ROPE, "gather": K_GATHER,

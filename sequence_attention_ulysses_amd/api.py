@@ -178,7 +178,8 @@ class UlyssesContext:
 
     # -- the exchange -----------------------------------------------------------
     def scatter_qkv(self, q=None, k=None, v=None, tags=("q", "k", "v"), out=None, stream=None):
-        """Sequence-sharded -> head-sharded for up to three operands, one launch on the comm stream.
+        """Sequence-sharded -> head-sharded for up to three operands, one launch (on the comm
+        stream, or on the caller's stream with the "caller" route, see :meth:`set_route`).
 
         Returns the destination tensors [P, B, P*S_l, H/P, D] (None for absent members).
         Pair with :meth:`wait` before consuming them.
@@ -482,8 +483,10 @@ class UlyssesContext:
         return h.value or 0
 
     def set_route(self, route: str) -> None:
-        """How scatter_qkv moves its operands: "kernel" (compute units) or "copy_engine"."""
-        code = {"kernel": _lib.ROUTE_KERNEL, "copy_engine": _lib.ROUTE_COPY_ENGINE}[route]
+        """How scatter_qkv moves its operands: "kernel" (compute units, comm stream),
+        "copy_engine" (copy engines, comm stream) or "caller" (compute units, caller stream)."""
+        code = {"kernel": _lib.ROUTE_KERNEL, "copy_engine": _lib.ROUTE_COPY_ENGINE,
+                "caller": _lib.ROUTE_CALLER}[route]
         check(self._lib.uly_set_route(self._h(), code), "uly_set_route")
 
     def debug_fail_launch(self, after: int = 0) -> None:

@@ -612,6 +612,12 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
             if (mem[i] && !ops[i].empty() && ops[i].S > 1 && ops[i].ss < (ops[i].H / c->P) * ops[i].D)
                 return fail(ULY_E_UNSUPPORTED, "%s: copy engines need a token pitch of at least one head band",
                             names[i]);
+    if (c->route == ULY_ROUTE_CALLER) {
+        // stream order on `caller` covers input readiness and target reuse
+        if ((st = launch(c, ULY_K_SCATTER, caller, [&] { launch_relayout(batch, false, caller); })) != ULY_OK)
+            return st;
+        return mark_pending(c, caller);
+    }
     if ((st = fork_comm(c, caller)) != ULY_OK) return st;
     if (c->route == ULY_ROUTE_COPY_ENGINE) {
         // One 2-D copy per (source rank, destination rank, batch) block, straight
@@ -1182,7 +1188,8 @@ uly_status uly_comm_stream(uly_ctx *c, hipStream_t *out) {
 uly_status uly_set_route(uly_ctx *c, int route) {
     uly_status st = ctx_ok(c);
     if (st != ULY_OK) return st;
-    if (route != ULY_ROUTE_KERNEL && route != ULY_ROUTE_COPY_ENGINE) return fail(ULY_E_INVAL, "bad route %d", route);
+    if (route != ULY_ROUTE_KERNEL && route != ULY_ROUTE_COPY_ENGINE && route != ULY_ROUTE_CALLER)
+        return fail(ULY_E_INVAL, "bad route %d", route);
     c->route = route;
     return ULY_OK;
 }

@@ -757,6 +757,18 @@ def test_copy_engine_route(dev, orc, P, B, S_l, Hq, Hkv, D, fused):
         torch.cuda.synchronize()
         for y, y2 in zip(ys, ys2):
             assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+        # the caller route: the same kernel on the caller's stream, no events; a
+        # consumer later on that stream sees the result without any wait
+        ctx.set_route("caller")
+        before = ctx.stats()["launches"]
+        ys3 = ctx.scatter_qkv(q, k, v, tags=("q3", "k3", "v3"))
+        sums = [y.float().sum() for y in ys3]         # consumer kernels on the same stream
+        ctx.wait()
+        torch.cuda.synchronize()
+        assert ctx.stats()["launches"] == before + 1
+        for y, y3, sm in zip(ys, ys3, sums):
+            assert torch.equal(y.view(torch.int16), y3.view(torch.int16))
+            assert torch.equal(sm, y.float().sum())
 
 
 # ---------------------------------------------------------------------------

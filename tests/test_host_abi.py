@@ -252,6 +252,18 @@ def test_fused_rejections(lib, ctx4):
     assert _fused(lib, ctx4, q, k2, v=v_over) == _lib.E_OVERLAP
 
 
+def test_route_arguments(lib, ctx4):
+    """Three routes for the plain scatter; anything else is refused and changes nothing."""
+    q = T(BASE, (1, 16, 8, 128))
+    for route in (_lib.ROUTE_KERNEL, _lib.ROUTE_COPY_ENGINE, _lib.ROUTE_CALLER):
+        assert lib.uly_set_route(ctx4.h, route) == _lib.OK
+        assert scatter(lib, ctx4, q=q, tags=(None, None, None), outs=(BASE + 64 * MiB, None, None)) == _lib.E_UNSUPPORTED
+        assert b"host-only" in lib.uly_last_error()
+    for bad in (-1, 3):
+        assert lib.uly_set_route(ctx4.h, bad) == _lib.E_INVAL
+    assert lib.uly_set_route(None, _lib.ROUTE_KERNEL) == _lib.E_INVAL
+
+
 def test_launch_size_limits(lib, ctx4):
     """Flat 32-bit indices cover 2^31 16-byte vectors (32 GiB) per operand plan, and
     2^31 rows per fused launch: larger calls are refused before anything is enqueued."""
