@@ -60,7 +60,8 @@
  * Streams.  The context owns one extra HIP stream ("comm stream", default
  *   priority) on which the plain Q/K/V scatter runs, so that it overlaps
  *   the fused Q/K norm + RoPE scatter enqueued on the caller's stream
- *   ([P27 "Changes Made": strided V submitted before Q/K norm and RoPE).
+ *   ([P27 "Changes Made": strided V submitted before Q/K norm and RoPE);
+ *   uly_set_route can move it onto the caller's stream instead.
  *   Before writing a target the comm stream waits for everything already
  *   enqueued on the caller's stream, so a consumer that read the previous
  *   contents on that stream is ordered before the overwrite.
@@ -139,7 +140,7 @@ uly_status uly_destroy(uly_ctx *ctx);
  * (tag, mode, dtype, per-rank shape, the context's device).  Per-rank shape
  * is [B, S, Hl, D] for ULY_MODE_SCATTER and [B, S_l, H, D] for
  * ULY_MODE_GATHER; the storage must hold P such slabs contiguously
- * (bytes >= P * B*S*Hl*D * 2) and be 16-byte aligned.  Fails with
+ * (bytes >= P * B*S*Hl*D * element size) and be 16-byte aligned.  Fails with
  * ULY_E_CACHE_FULL when max_targets keys exist (there is no eviction: an
  * evicted target could still be referenced by a caller) and ULY_E_INVAL
  * when the key is already registered.  tag: NUL-terminated, <= 63 bytes. */
