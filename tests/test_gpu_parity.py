@@ -801,7 +801,8 @@ def test_byte_payloads_bit_exact(dev, orc, P, B, S_l, Hq, Hkv, D):
 
 @pytest.mark.parametrize("P,B,S_l,H,D,dtype,fused", [(4, 1, 200, 24, 128, "bf16", True), (2, 1, 128, 8, 64, "f16", False),
                                                      (2, 2, 37, 6, 128, "bf16", False), (4, 1, 29, 8, 32, "bf16", True),
-                                                     (2, 1, 50, 4, 256, "f16", False)])
+                                                     (2, 1, 50, 4, 256, "f16", False),
+                                                     (4, 1, 4096, 24, 128, "bf16", True)])   # the video-DiT block
 def test_packed_receive_layout(dev, orc, P, B, S_l, H, D, dtype, fused):
     """flashinfer PR #6332, 'Description' (Layouts): the fused [B, S, Hl, 3D] payload
     holds q, k and v side by side in every head row."""
