@@ -691,7 +691,7 @@ def _random_case(rng):
     return P, B, S_l, P * Hl_q, P * Hl_k, D, dtype, pad
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_shapes_all_paths(dev, orc, seed):
     """Random world sizes, head counts, head dims, tails, dtypes and source row
     padding through the plain scatter, the fused norm + RoPE scatter (with V) and
