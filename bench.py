@@ -359,9 +359,10 @@ WORKLOADS = {"video_dit": setup_video_dit, "wan_long": setup_wan_long, "gqa": se
 def measure_protocol(args, torch, dev, setup, step, timed, samples: int = 100):
     """The rest of the timing protocol, outside the timed region: the spread
     of single steps (events on the stream every kernel of the step runs on),
-    an A/A repeat of the timed loop, a plain device copy of the step's bytes,
-    and the same step in fp16 (a relayout moves bytes, so the rate must not
-    depend on the 16-bit type)."""
+    an A/A repeat of the timed loop, a plain device copy of the step's bytes
+    (torch's, and the library's own relayout kernel as an identity copy: the
+    copy roof of this box), and the same step in fp16 (a relayout moves bytes,
+    so the rate must not depend on the 16-bit type)."""
     from sequence_attention_ulysses_amd import UlyssesContext, rope_table_1d, synth
 
     nbytes = setup["bytes_per_step"]
@@ -387,13 +388,30 @@ def measure_protocol(args, torch, dev, setup, step, timed, samples: int = 100):
             "GB_s": round(nbytes / (wall / args.steps) / 1e9, 2)}
     del src, dst
 
+    # the same bytes through the library's own relayout kernel as a plain copy
+    # (one rank: the identity map), on the caller's stream: this box's copy roof
+    rows = (nbytes // 2) // (128 * 128 * 2)
+    csrc = torch.ones((1, 1, rows, 128, 128), dtype=torch.bfloat16, device=dev)
+    cdst = torch.empty_like(csrc)
+    with UlyssesContext(1, device=0) as cctx:
+        cctx.set_route("caller")
+        for _ in range(args.warmup):
+            cctx.scatter_qkv(q=csrc, out=(cdst, None, None))
+        wall = timed(lambda: cctx.scatter_qkv(q=csrc, out=(cdst, None, None)), args.steps)
+    cbytes = 2 * csrc.numel() * 2
+    copy_roof = {"kernel": "relayout_kernel, one rank (identity map)", "bytes_moved": cbytes,
+                 "us": round(wall * 1e6 / args.steps, 2), "GB_s": round(cbytes / (wall / args.steps) / 1e9, 1)}
+    del csrc, cdst
+
     f16 = setup_video_dit(torch, dev, synth, rope_table_1d, UlyssesContext, dtype="f16")
     for _ in range(args.warmup):
         f16["step"]()
     wall = timed(f16["step"], args.steps)
     f16["ctx"].close()
     fp16 = {"ms_per_step": round(wall * 1e3 / args.steps, 5), "GB_s": round(nbytes / (wall / args.steps) / 1e9, 2)}
-    return {"step_spread": spread, "aa_repeat": aa, "device_copy_control": copy, "fp16_same_shape": fp16}
+    copy_roof["step_over_copy_roof"] = round(aa["GB_s"] / copy_roof["GB_s"], 4)
+    return {"step_spread": spread, "aa_repeat": aa, "device_copy_control": copy, "copy_roof": copy_roof,
+            "fp16_same_shape": fp16}
 
 
 def calibrate_copy(args, torch, UlyssesContext):
