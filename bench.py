@@ -440,7 +440,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
-                    help="also time each step after a 1 GiB scrub of the caches (event-timed, reported apart)")
+                    help="also time each step after a 1 GiB read that evicts the caches (event-timed, reported apart)")
     ap.add_argument("--no-profile", action="store_true", help="do not bracket launches with timing events")
     ap.add_argument("--no-two-stream", action="store_true",
                     help="skip the two-stream comparison (profiling runs then hold only the headline step)")
@@ -547,11 +547,17 @@ def main():
 
     cold = None
     if args.cold:
-        scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # Reading 1 GiB evicts the L2s and the 256 MB Infinity Cache without
+        # leaving dirty lines whose write-back would overlap the timed step.
+        scrub = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+        torch.cuda.synchronize()
         times = []
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for _ in range(20):
-            scrub.fill_(1)
+            # no wait between the scrub and the step: the host enqueues the
+            # step while the scrub runs, so the events time the GPU, not the
+            # host's launch latency
+            scrub.max()
             e0.record()
             step()
             e1.record()
@@ -562,6 +568,25 @@ def main():
         cold = {"median_ms": round(med, 4),
                 unit.replace("/", "_"): round(args.bytes_per_step / (med * 1e-3) / unit_div, 1),
                 "p10_ms": round(times[2], 4), "p90_ms": round(times[17], 4)}
+        # the same cold steps again, each kernel bracketed by the library's own events
+        if not args.no_profile:
+            ctx.profile(True, every=1)
+            ctx.profile_reset()
+            for _ in range(20):
+                scrub.max()
+                torch.cuda.synchronize()
+                step()
+                torch.cuda.synchronize()
+            per_kernel = {}
+            from sequence_attention_ulysses_amd._lib import KERNEL_KINDS
+            for kind in KERNEL_KINDS:
+                ms, n = ctx.profile_read(kind)
+                if n:
+                    per_kernel[kind] = round(ms * 1e3 / n, 2)
+            ctx.profile(False)
+            ctx.profile_reset()
+            cold["kernel_avg_us"] = per_kernel
+        del scrub
 
     extra = measure_protocol(args, torch, dev, setup, step, timed) if args.workload == "video_dit" else None
 
