@@ -23,9 +23,13 @@
 // leave the matrix cores idle through every epilogue; measured slower.)
 //
 // Operands go global -> LDS with global_load_lds_dwordx4 (no staging
-// registers, no ds_write) into a ring of K stages; the loads of later stages
-// are in flight while a stage is multiplied.  LDS rows are XOR-swizzled so
-// the 16-byte fragment reads do not collide on banks.
+// registers, no ds_write) into a two-stage ring of 64-wide K stages; the
+// next stage's loads are in flight while a stage is multiplied.  LDS rows are
+// XOR-swizzled so the 16-byte fragment reads do not collide on banks.  The
+// main loop's instruction order is fixed by hand (scheduling barriers): each
+// product is followed by at most one fragment read of the next K step and
+// one load of the next stage, and a stage's last K step is multiplied after
+// the next barrier, while the next stage's first fragments are read.
 //
 // Epilogue: the block's 256 cos/sin table rows are first staged into LDS in
 // one coalesced pass (as interleaved (cos, sin) pairs, rows padded by 16
@@ -58,11 +62,7 @@ constexpr int kWavesPerSimd = kWaves / 4;                // occupancy: one block
 static_assert(kChunks == 4 || kChunks == 8, "LDS rows of 64 or 128 bytes");
 static_assert(kWaves == kProjHeads * kWavesT && (kWaveT == 64 || kWaveT == 128), "wave grid");
 
-#ifndef ULY_PROJ_STAGES
-#define ULY_PROJ_STAGES 2
-#endif
-constexpr int kStages = ULY_PROJ_STAGES;
-static_assert(kStages >= 2, "a ring of at least two stages");
+constexpr int kStages = 2;                               // LDS ring: the stage in use and the next
 constexpr int kSlotsA = kRowsA * kChunks, kSlotsB = kRowsB * kChunks;   // 16-byte slots per stage
 constexpr int kInstA = kSlotsA / 64 / kWaves, kInstB = kSlotsB / 64 / kWaves;   // loads per wave per stage
 static_assert(kSlotsA % (64 * kWaves) == 0 && kSlotsB % (64 * kWaves) == 0, "whole wave instructions");
@@ -116,24 +116,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VM) : "memory");
 }
 
-// Wait until at most min(N, later) stages of PER loads each are outstanding.
-template <int N, int PER>
-__device__ __forceinline__ void wait_stages(uint32_t later) {
-    if constexpr (N == 0) {
-        wait_vmcnt<0>();
-    } else {
-        if (later >= uint32_t(N)) wait_vmcnt<N * PER>();
-        else wait_stages<N - 1, PER>(later);
-    }
-}
-
 #ifndef ULY_PROJ_GROUP
 #define ULY_PROJ_GROUP 4
 #endif
-#ifndef ULY_PROJ_SPREAD
-#define ULY_PROJ_SPREAD 1
+#ifndef ULY_PROJ_LOAD_KS
+#define ULY_PROJ_LOAD_KS 2
 #endif
-constexpr bool kSpread = ULY_PROJ_SPREAD;
 
 // Block -> (token tile, head block).  Workgroups go to the 8 XCDs round
 // robin (block b to XCD b % 8) and each XCD has its own L2.  The grid is cut
@@ -370,16 +358,12 @@ void proj_kernel(ProjArgs a) {
     const uint32_t wu = __builtin_amdgcn_readfirstlane(uint32_t(wv));
     const uint32_t wA = wu * kInstA * 64 * 16;
     const uint32_t wB = kSlotsA * 16 + wu * kInstB * 64 * 16;
-    // Part `part` of `parts` of the loads of stage kt into ring slot st.
-    auto issue = [&](uint32_t kt, uint32_t st, int part, int parts) {
+    // Load instruction u (A rows first, then B rows) of stage kt into ring slot st.
+    auto load_one = [&](uint32_t kt, uint32_t st, int u) {
         const uint32_t k0 = kt * (kProjTileK / 8);
         const uint32_t sb = ring + st * (kSlotsA + kSlotsB) * 16;
-#pragma unroll
-        for (int u = 0; u < kInstA; ++u)
-            if (u * parts / kInstA == part) dma16(wq + offA[u] + k0, sb + wA + u * 64 * 16);
-#pragma unroll
-        for (int u = 0; u < kInstB; ++u)
-            if (u * parts / kInstB == part) dma16(xq + offB[u] + k0, sb + wB + u * 64 * 16);
+        if (u < kInstA) dma16(wq + offA[u] + k0, sb + wA + u * 64 * 16);
+        else dma16(xq + offB[u - kInstA] + k0, sb + wB + (u - kInstA) * 64 * 16);
     };
 
     f32x16_t acc[4][kTB];
@@ -390,40 +374,96 @@ void proj_kernel(ProjArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
 
-    const uint32_t KT = a.K / kProjTileK;
+    const uint32_t KT = a.K / kProjTileK;              // >= 1: the host requires K % 64 == 0, K > 0
+    constexpr int kPer = kInstA + kInstB;              // this wave's load instructions per stage
 #pragma unroll
-    for (int p = 0; p < kStages - 1; ++p)
-        if (uint32_t(p) < KT) issue(p, p, 0, 1);
+    for (int u = 0; u < kPer; ++u) load_one(0, 0, u);
     const int fr = lane & 31;          // fragment row (A) / column (B) of this lane
     const int fk = lane >> 5;          // which 8-wide half of a 16-wide K step
-    constexpr int kPer = kInstA + kInstB;
+    // Main loop, in a fixed instruction order.  Each K step issues its
+    // products one by one, with one fragment read of the next K step after
+    // each of the first 4+kTB products and this wave's loads of the next
+    // stage spread over the products of the first kLoadKs steps.  The last K
+    // step of a stage is read before the next barrier and multiplied after
+    // it, so its products cover the LDS reads that open the next stage, and
+    // the next stage's loads go out right after the barrier.  The loads are
+    // unconditional: the last stage loads itself again into the free slot (in
+    // bounds), and the epilogue waits for those before it reuses the ring.
+    // (Left to the compiler, the reads of a step were issued after most of
+    // the products that could cover them.)
+    constexpr int KS = kProjTileK / 16;
+    constexpr int kM = 4 * kTB;                                   // products per K step
+    constexpr int kR = 4 + kTB;                                   // fragment reads per K step
+    constexpr int kLoadKs = ULY_PROJ_LOAD_KS < KS - 1 ? ULY_PROJ_LOAD_KS : KS - 1;
+    constexpr int kLPer = (kPer + kLoadKs - 1) / kLoadKs;         // loads per loading step
+    static_assert(kR <= kM && kLPer <= kM, "schedule shape");
+    auto read_frag = [&](const uint4 *sa, const uint4 *sb, int ks, int r, uint4 (&fa)[4], uint4 (&fb)[kTB]) {
+        const int c = ks * 2 + fk;
+        if (r < 4) fa[r] = sa[swz(wn * kProjD + r * 32 + fr, c)];
+        else fb[r - 4] = sb[swz(wt * kWaveT + (r - 4) * 32 + fr, c)];
+    };
+#define ULY_SB() __builtin_amdgcn_sched_barrier(0)
+    // Products of (fa, fb); reads of K step `rks` (if >= 0) into (na, nb);
+    // loads lbase .. lbase+lcount-1 of stage kn into slot sn.
+    auto kstep = [&](const uint4 (&fa)[4], const uint4 (&fb)[kTB], uint4 (&na)[4], uint4 (&nb)[kTB],
+                     const uint4 *sa, const uint4 *sb, int rks, int lbase, int lcount, uint32_t kn, uint32_t sn) {
+#pragma unroll
+        for (int i = 0; i < kM; ++i) {
+            acc[i / kTB][i % kTB] = mfma<DT>(fa[i / kTB], fb[i % kTB], acc[i / kTB][i % kTB]);
+            ULY_SB();
+            if (rks >= 0 && i < kR) {
+                read_frag(sa, sb, rks, i, na, nb);
+                ULY_SB();
+            }
+            if (lcount > 0) {
+                const int l0 = (i * lcount) / kM, l1 = ((i + 1) * lcount) / kM;
+                if (l1 != l0) {
+                    load_one(kn, sn, lbase + l0);
+                    ULY_SB();
+                }
+            }
+        }
+    };
+    uint4 fa[4], fb[kTB], ga[4], gb[kTB];
     for (uint32_t kt = 0; kt < KT; ++kt) {
         const uint32_t st = kt % kStages;
-        // this wave's loads of stage kt are done once at most the later
-        // stages' loads (kt+1 .. kt+kStages-2 where they exist) are outstanding
-        wait_stages<kStages - 2, kPer>(KT - 1 - kt);
-        lds_barrier();     // every wave's stage kt landed; every wave is done with stage kt-1
-        const bool more = kt + kStages - 1 < KT;
-        const uint32_t kn = kt + kStages - 1, sn = (kt + kStages - 1) % kStages;
-        if (!kSpread && more) issue(kn, sn, 0, 1);
+        wait_vmcnt<0>();
+        lds_barrier();
+        const uint32_t kn = min(kt + 1, KT - 1), sn = (kt + 1) % kStages;
         const uint4 *sa = lds + st * (kSlotsA + kSlotsB), *sb = sa + kSlotsA;
-        constexpr int KS = kProjTileK / 16;
+        // multiply steps of this iteration: m = 0 is the carried last step of
+        // the previous stage (none at kt = 0, where step 0 is read first)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int c = ks * 2 + fk;
-            uint4 fa[4], fb[kTB];
+        for (int m = 0; m < KS; ++m) {
+            // step m reads K step m of this stage and multiplies the fragments
+            // of the step before it: the carried one for m = 0.  Even steps
+            // multiply (fa, fb) and read into (ga, gb), odd steps the reverse.
+            const int lb = m * kLPer, lc = m < kLoadKs ? (kPer - lb < kLPer ? kPer - lb : kLPer) : 0;
+            if (kt == 0 && m == 0) {
+                // nothing carried into the first stage: read step 0 where step
+                // 1 expects it and issue this step's loads on their own
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) fa[nb] = sa[swz(wn * kProjD + nb * 32 + fr, c)];
+                for (int r = 0; r < kR; ++r) read_frag(sa, sb, 0, r, ga, gb);
 #pragma unroll
-            for (int tb = 0; tb < kTB; ++tb) fb[tb] = sb[swz(wt * kWaveT + tb * 32 + fr, c)];
-            // the next stage's loads, spread over the K steps between the products
-            if (kSpread && more) issue(kn, sn, ks, KS);
+                for (int l = 0; l < lc; ++l) load_one(kn, sn, lb + l);
+                ULY_SB();
+                continue;
+            }
+            if ((m & 1) == 0) kstep(fa, fb, ga, gb, sa, sb, m, lb, lc, kn, sn);
+            else kstep(ga, gb, fa, fb, sa, sb, m, lb, lc, kn, sn);
+        }
+        // step KS-1 read into (fa, fb) if KS-1 is odd, else into (ga, gb):
+        // keep it in (fa, fb) for the carry
+        if ((KS & 1) == 1) {
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int i = 0; i < 4; ++i) fa[i] = ga[i];
 #pragma unroll
-                for (int tb = 0; tb < kTB; ++tb) acc[nb][tb] = mfma<DT>(fa[nb], fb[tb], acc[nb][tb]);
+            for (int i = 0; i < kTB; ++i) fb[i] = gb[i];
         }
     }
+    if (KT > 0) kstep(fa, fb, ga, gb, nullptr, nullptr, -1, 0, 0, 0, 0);
+#undef ULY_SB
+    wait_vmcnt<0>();      // the last stage's repeat loads land before the ring is reused
 
     // The ring is free once every wave is past its last stage: stage the
     // block's table rows there (only blocks with a q or k head rotate).

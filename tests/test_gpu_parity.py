@@ -870,6 +870,7 @@ PROJ_SMALL = [
     (4, 2, 64, 384, 4, 4, "bf16"),       # B = 2, six K stages
     (8, 1, 32, 1024, 8, 8, "bf16"),
     (2, 1, 300, 192, 2, 2, "f16"),       # three K stages
+    (1, 1, 70, 64, 3, 1, "bf16"),        # one K stage, five heads (last head block half empty)
 ]
 
 
