@@ -227,11 +227,20 @@ __device__ __forceinline__ void stage_table(const ProjArgs &a, uint32_t m0, floa
     }
 }
 
-// The epilogue of wave (wn, wt): RMSNorm + RoPE of q/k rows (v as is), one
-// rounding, and the stores into the head-sharded targets.
+// The sum of x over lane l and lane l ^ 32: v_permlane32_swap of x with
+// itself yields, in its two results, x of the lane 32 below (upper half) and
+// of the lane 32 above (lower half), each beside the lane's own x.
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The epilogue of wave (wn, wt): RMSNorm + RoPE of q/k rows (QK), or v as
+// is, one rounding, and the stores into the head-sharded targets.  The head
+// (and so QK) is wave-uniform: each wave runs one straight-line body.
 // acc[nb][tb][i] is column n = 32nb + 8(i/4) + 4*half + i%4 (the head-dim
-// index d) of token m0 + 128wt + 32tb + lane%32 and head `hd`.
-template <int DT>
+// index d) of token m0 + kWaveT*wt + 32tb + lane%32 and head `hd`.
+template <int DT, bool QK>
 __device__ __forceinline__ void proj_epilogue(const ProjArgs &a, f32x16_t (&acc)[4][kTB], uint32_t m0,
                                               uint32_t hd, int wt, int lane, const float4 *tbl) {
     const uint32_t half = lane >> 5;
@@ -242,14 +251,20 @@ __device__ __forceinline__ void proj_epilogue(const ProjArgs &a, f32x16_t (&acc)
     uint16_t *dbase = a.dst[comp] + int64_t(qd) * a.d_q[comp] + int64_t(jd) * kProjD;
     const int64_t d_b = a.d_b[comp], d_g = a.d_g[comp];
 
-    // this lane's 64 norm weights, d = 32nb + 8grp + 4half + 0..3, kept packed
-    uint2 wr[4][4];
-    if (comp < 2) {
+    // this lane's 64 norm weights, d = 32nb + 8grp + 4half + 0..3, widened once
+    float wf[4][4][4];
+    if constexpr (QK) {
         const uint16_t *wn = a.wn[comp];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp) wr[nb][grp] = *(const uint2 *)(wn + nb * 32 + grp * 8 + half * 4);
+            for (int grp = 0; grp < 4; ++grp) {
+                const uint2 w4 = *(const uint2 *)(wn + nb * 32 + grp * 8 + half * 4);
+                wf[nb][grp][0] = widen1<DT>(w4.x & 0xFFFFu);
+                wf[nb][grp][1] = widen1<DT>(w4.x >> 16);
+                wf[nb][grp][2] = widen1<DT>(w4.y & 0xFFFFu);
+                wf[nb][grp][3] = widen1<DT>(w4.y >> 16);
+            }
     }
 
 #pragma unroll
@@ -260,53 +275,60 @@ __device__ __forceinline__ void proj_epilogue(const ProjArgs &a, f32x16_t (&acc)
         uint32_t b;
         const uint32_t g = token_pos(a, live ? tok : a.M - 1, b);
         float inv = 1.f;
-        if (comp < 2) {
+        if constexpr (QK) {
             float ss = 0.f;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) ss = fmaf(acc[nb][tb][i], acc[nb][tb][i], ss);
-            ss += __shfl_xor(ss, 32, 64);
             // eps > 0 keeps the argument normal: the bare reciprocal square root suffices
-            inv = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_D, a.eps));
+            inv = __builtin_amdgcn_rsqf(fmaf(sum_halves(ss), a.inv_D, a.eps));
         }
         uint16_t *drow = dbase + int64_t(b) * d_b + int64_t(g) * d_g;
         const float4 *trow = tbl + tl * kTblRow;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             uint32_t pk[8];   // pk[2*grp + p]: the pair (d0 + 2p, d0 + 2p + 1) of register group grp
+            if constexpr (QK) {
+                // pairs j0 = 16nb + 4grp + 2half and j0 + 1: chunk j0 / 2 of the row
+                float4 cs[4];
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                if (comp < 2) {
-                    // pairs j0 = 16nb + 4grp + 2half and j0 + 1: chunk j0 / 2 of the row
-                    const float4 cs = trow[nb * 8 + grp * 2 + half];
-                    const float cv[2] = {cs.x, cs.z}, sv[2] = {cs.y, cs.w};
-                    const uint32_t wp[2] = {wr[nb][grp].x, wr[nb][grp].y};
+                for (int grp = 0; grp < 4; ++grp) cs[grp] = trow[nb * 8 + grp * 2 + half];
+#pragma unroll
+                for (int grp = 0; grp < 4; ++grp) {
+                    const float cv[2] = {cs[grp].x, cs[grp].z}, sv[2] = {cs[grp].y, cs[grp].w};
 #pragma unroll
                     for (int p = 0; p < 2; ++p) {
                         const int i0 = grp * 4 + p * 2;
-                        const float n0 = acc[nb][tb][i0] * inv * widen1<DT>(wp[p] & 0xFFFFu);
-                        const float n1 = acc[nb][tb][i0 + 1] * inv * widen1<DT>(wp[p] >> 16);
+                        const float n0 = acc[nb][tb][i0] * inv * wf[nb][grp][2 * p];
+                        const float n1 = acc[nb][tb][i0 + 1] * inv * wf[nb][grp][2 * p + 1];
                         pk[grp * 2 + p] = pack2<DT>(n0 * cv[p] - n1 * sv[p], n0 * sv[p] + n1 * cv[p]);
                     }
-                } else {
+                }
+            } else {
+#pragma unroll
+                for (int grp = 0; grp < 4; ++grp)
 #pragma unroll
                     for (int p = 0; p < 2; ++p)
                         pk[grp * 2 + p] = pack2<DT>(acc[nb][tb][grp * 4 + p * 2], acc[nb][tb][grp * 4 + p * 2 + 1]);
-                }
             }
             // Lane half 0 holds d runs {0-3, 8-11, 16-19, 24-27} (+32nb), half 1 the
-            // runs 4 higher; one exchange gives half 0 d 0-7 and 16-23, half 1 d 8-15
-            // and 24-31, each a 16-byte run.
-            uint32_t snd[4], rcv[4];
-            snd[0] = half ? pk[0] : pk[2];
-            snd[1] = half ? pk[1] : pk[3];
-            snd[2] = half ? pk[4] : pk[6];
-            snd[3] = half ? pk[5] : pk[7];
+            // runs 4 higher.  v_permlane32_swap trades the upper half-wave of its
+            // first operand for the lower half-wave of its second: swapping run
+            // 0-3 with run 8-11 (and 16-19 with 24-27) leaves half 0 with d 0-7
+            // and 16-23 and half 1 with d 8-15 and 24-31, in the same registers,
+            // each a 16-byte run.
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rcv[i] = __shfl_xor(snd[i], 32, 64);
-            const uint4 lo = half ? make_uint4(rcv[0], rcv[1], pk[2], pk[3]) : make_uint4(pk[0], pk[1], rcv[0], rcv[1]);
-            const uint4 hi = half ? make_uint4(rcv[2], rcv[3], pk[6], pk[7]) : make_uint4(pk[4], pk[5], rcv[2], rcv[3]);
+            for (int i = 0; i < 2; ++i) {
+                const auto r0 = __builtin_amdgcn_permlane32_swap(pk[i], pk[2 + i], false, false);
+                pk[i] = r0[0];
+                pk[2 + i] = r0[1];
+                const auto r1 = __builtin_amdgcn_permlane32_swap(pk[4 + i], pk[6 + i], false, false);
+                pk[4 + i] = r1[0];
+                pk[6 + i] = r1[1];
+            }
+            const uint4 lo = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            const uint4 hi = make_uint4(pk[4], pk[5], pk[6], pk[7]);
             if (live) {
                 stg16(drow + nb * 32 + half * 8, lo);
                 stg16(drow + nb * 32 + 16 + half * 8, hi);
@@ -324,7 +346,7 @@ void proj_kernel(ProjArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave-uniform, so per-head choices are scalar
     const int wn = wv / kWavesT;       // head of the block this wave computes
     const int wt = wv % kWavesT;       // token slice of the block this wave computes
     uint32_t tile, hb;
@@ -474,7 +496,8 @@ void proj_kernel(ProjArgs a) {
         lds_barrier();
     }
     const uint32_t hd = head0 + wn;
-    if (hd < a.NH) proj_epilogue<DT>(a, acc, m0, hd, wt, lane, tbl);
+    if (hd < a.Hq + a.Hkv) proj_epilogue<DT, true>(a, acc, m0, hd, wt, lane, tbl);
+    else if (hd < a.NH) proj_epilogue<DT, false>(a, acc, m0, hd, wt, lane, tbl);
 }
 
 }  // namespace
