@@ -14,13 +14,13 @@
 // one lane's registers; one more exchange with lane ^ 32 turns the runs of 4
 // into 16-byte runs for the stores.
 //
-// Tiling: a block of 8 waves owns two heads (256 output columns; each head
+// Tiling: a block of 4 waves owns two heads (256 output columns; each head
 // is one component q, k or v) and 256 tokens.  Wave (wn, wt) owns head wn
-// and tokens [64wt, 64wt+64): a 128 x 64 tile of 4 x 2 MFMA blocks, 128
-// fp32 accumulators per lane, so two waves fit on each SIMD and one wave's
-// epilogue and barriers overlap the other's products.  (128-token waves,
-// 256 accumulators and one wave per SIMD, read less LDS per product but
-// leave the matrix cores idle through every epilogue; measured slower.)
+// and tokens [128wt, 128wt+128): a 128 x 128 tile of 4 x 4 MFMA blocks, 256
+// fp32 accumulators per lane (in the accumulation registers), one wave per
+// SIMD.  Per product it reads 2/3 of the LDS bytes that 8 waves of 128 x 64
+// (two per SIMD) read; those let one wave's epilogue overlap the other's
+// products but measured ~2 % slower.  Both shapes build (ULY_PROJ_WAVE_T).
 //
 // Operands go global -> LDS with global_load_lds_dwordx4 (no staging
 // registers, no ds_write) into a two-stage ring of 64-wide K stages; the
@@ -120,7 +120,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 #define ULY_PROJ_GROUP 4
 #endif
 #ifndef ULY_PROJ_LOAD_KS
-#define ULY_PROJ_LOAD_KS 2
+#define ULY_PROJ_LOAD_KS 3
 #endif
 
 // Block -> (token tile, head block).  Workgroups go to the 8 XCDs round
