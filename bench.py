@@ -442,6 +442,9 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time each step after a 1 GiB read that evicts the caches (event-timed, reported apart)")
     ap.add_argument("--no-profile", action="store_true", help="do not bracket launches with timing events")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step into a HIP graph and time its replays (no per-launch host work; "
+                         "implies --no-profile and --no-two-stream)")
     ap.add_argument("--no-two-stream", action="store_true",
                     help="skip the two-stream comparison (profiling runs then hold only the headline step)")
     ap.add_argument("--route", choices=("kernel", "copy_engine", "caller"), default=None,
@@ -490,6 +493,9 @@ def main():
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
+    if args.graph:
+        args.no_profile = args.no_two_stream = True
+        step_per_operator = None
     for _ in range(args.warmup):
         step()
         if not args.no_two_stream:
@@ -497,6 +503,23 @@ def main():
         if step_per_operator is not None:
             step_per_operator()
     torch.cuda.synchronize()
+    if args.graph:
+        # the library's calls are capturable: its targets are registered and its
+        # event pools filled by the warmup steps, and a step allocates nothing
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            step()
+        torch.cuda.synchronize()
+        step = graph.replay
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        setup["config"]["launch"] = "hip_graph"
     dom_kind, dom_bytes, dom_name = setup["dominant"][:3]
     dom_bound, dom_peak, dom_unit = (setup["dominant"][3:] if len(setup["dominant"]) > 3
                                      else ("hbm", HBM_PEAK_GBS, "GB/s"))
@@ -588,7 +611,8 @@ def main():
             cold["kernel_avg_us"] = per_kernel
         del scrub
 
-    extra = measure_protocol(args, torch, dev, setup, step, timed) if args.workload == "video_dit" else None
+    extra = (measure_protocol(args, torch, dev, setup, step, timed)
+             if args.workload == "video_dit" and not args.graph else None)
 
     ctx.close()
 
