@@ -47,6 +47,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u32x4_t global_u32x4_t;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -56,7 +57,15 @@ constexpr int kChunks = kProjTileK / 8;                  // 16-byte chunks per L
 constexpr int kRowsA = kProjHeads * kProjD;              // weight rows per block
 constexpr int kRowsB = kProjTileT;                       // token rows per block
 constexpr int kWaveT = kProjWaveT;                       // tokens per wave
-constexpr int kTB = kWaveT / 32;                         // 32-token MFMA blocks per wave
+#ifndef ULY_PROJ_MFMA
+#define ULY_PROJ_MFMA 16
+#endif
+constexpr int kMf = ULY_PROJ_MFMA;                       // MFMA block edge: 16 (16x16x32) or 32 (32x32x16)
+static_assert(kMf == 16 || kMf == 32, "MFMA shape");
+constexpr int kKStep = 512 / kMf;                        // K per product
+constexpr int kNB = kProjD / kMf;                        // head-dim blocks per wave
+constexpr int kTB = kWaveT / kMf;                        // token blocks per wave
+typedef float accv_t __attribute__((ext_vector_type(kMf * kMf / 64)));   // one block's accumulators per lane
 constexpr int kWavesT = kProjTileT / kWaveT;             // waves along the tokens
 constexpr int kWavesPerSimd = kWaves / 4;                // occupancy: one block per CU
 static_assert(kChunks == 4 || kChunks == 8, "LDS rows of 64 or 128 bytes");
@@ -157,13 +166,22 @@ __device__ __forceinline__ int swz_key(int row) { return (row >> (ULY_PROJ_SWZ))
 __device__ __forceinline__ int swz(int row, int c) { return row * kChunks + (c ^ swz_key(row)); }
 
 template <int DT>
-__device__ __forceinline__ f32x16_t mfma(uint4 a, uint4 b, f32x16_t c) {
+__device__ __forceinline__ accv_t mfma(uint4 a, uint4 b, accv_t c) {
+#if ULY_PROJ_MFMA == 32
     if constexpr (DT == 2)
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                       __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+#else
+    if constexpr (DT == 2)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+#endif
 }
 
 template <int DT>
@@ -241,7 +259,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 // acc[nb][tb][i] is column n = 32nb + 8(i/4) + 4*half + i%4 (the head-dim
 // index d) of token m0 + kWaveT*wt + 32tb + lane%32 and head `hd`.
 template <int DT, bool QK>
-__device__ __forceinline__ void proj_epilogue(const ProjArgs &a, f32x16_t (&acc)[4][kTB], uint32_t m0,
+__device__ __forceinline__ void proj_epilogue(const ProjArgs &a, accv_t (&acc)[kNB][kTB], uint32_t m0,
                                               uint32_t hd, int wt, int lane, const float4 *tbl) {
     const uint32_t half = lane >> 5;
     const int comp = hd < a.Hq ? 0 : (hd < a.Hq + a.Hkv ? 1 : 2);
@@ -337,6 +355,107 @@ __device__ __forceinline__ void proj_epilogue(const ProjArgs &a, f32x16_t (&acc)
     }
 }
 
+// The sum of x over the four rows of 16 lanes that hold lane l % 16's
+// token: v_permlane16_swap of x with itself pairs rows 0-1 and 2-3 (each
+// lane gets its own row's x beside the partner row's), then the halves.
+// Every lane of the token adds in the same order.
+__device__ __forceinline__ float sum_rows4(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return sum_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+// The epilogue for 16 x 16 blocks, as proj_epilogue: acc[nb][tb][r] is
+// head-dim index d = 16nb + 4q + r (q = lane / 16, the lane's row) of token
+// m0 + kWaveT*wt + 16tb + lane%16.  A lane holds both rotation pairs of its
+// run of 4; the row's sum of squares is reduced over the token's four lane
+// rows.  For the stores, the runs of two head-dim blocks are traded across
+// rows (v_permlane32_swap, then v_permlane16_swap) so that row q writes 16
+// bytes of one of them: each store instruction covers 16 tokens x 64 bytes.
+template <int DT, bool QK>
+__device__ __forceinline__ void proj_epilogue16(const ProjArgs &a, accv_t (&acc)[kNB][kTB], uint32_t m0,
+                                                uint32_t hd, int wt, int lane, const float4 *tbl) {
+    const uint32_t q = lane >> 4;
+    const int comp = hd < a.Hq ? 0 : (hd < a.Hq + a.Hkv ? 1 : 2);
+    const uint32_t hc = hd - (comp == 0 ? 0u : (comp == 1 ? a.Hq : a.Hq + a.Hkv));
+    uint32_t qd, jd;
+    a.hl[comp].divmod(hc, qd, jd);
+    uint16_t *dbase = a.dst[comp] + int64_t(qd) * a.d_q[comp] + int64_t(jd) * kProjD;
+    const int64_t d_b = a.d_b[comp], d_g = a.d_g[comp];
+
+    // this lane's 32 norm weights, d = 16nb + 4q + 0..3, widened once
+    float wf[kNB][4];
+    if constexpr (QK) {
+        const uint16_t *wn = a.wn[comp];
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+            const uint2 w4 = *(const uint2 *)(wn + nb * 16 + q * 4);
+            wf[nb][0] = widen1<DT>(w4.x & 0xFFFFu);
+            wf[nb][1] = widen1<DT>(w4.x >> 16);
+            wf[nb][2] = widen1<DT>(w4.y & 0xFFFFu);
+            wf[nb][3] = widen1<DT>(w4.y >> 16);
+        }
+    }
+
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) {
+        const int tl = wt * kWaveT + tb * 16 + (lane & 15);   // token within the block tile
+        const uint32_t tok = m0 + tl;
+        const bool live = tok < a.M;
+        uint32_t b;
+        const uint32_t g = token_pos(a, live ? tok : a.M - 1, b);
+        float inv = 1.f;
+        if constexpr (QK) {
+            float ss = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ss = fmaf(acc[nb][tb][r], acc[nb][tb][r], ss);
+            // eps > 0 keeps the argument normal: the bare reciprocal square root suffices
+            inv = __builtin_amdgcn_rsqf(fmaf(sum_rows4(ss), a.inv_D, a.eps));
+        }
+        uint16_t *drow = dbase + int64_t(b) * d_b + int64_t(g) * d_g;
+        const float4 *trow = tbl + tl * kTblRow;
+#pragma unroll
+        for (int nbp = 0; nbp < kNB / 2; ++nbp) {
+            uint32_t X[2], Y[2];   // the run of head-dim blocks 2nbp (X) and 2nbp+1 (Y), two pairs each
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int nb = 2 * nbp + h;
+                uint32_t pk[2];
+                if constexpr (QK) {
+                    // pairs j0 = 8nb + 2q and j0 + 1: chunk j0 / 2 of the row
+                    const float4 cs = trow[4 * nb + q];
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        const float cv = p ? cs.z : cs.x, sv = p ? cs.w : cs.y;
+                        const float n0 = acc[nb][tb][2 * p] * inv * wf[nb][2 * p];
+                        const float n1 = acc[nb][tb][2 * p + 1] * inv * wf[nb][2 * p + 1];
+                        pk[p] = pack2<DT>(n0 * cv - n1 * sv, n0 * sv + n1 * cv);
+                    }
+                } else {
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) pk[p] = pack2<DT>(acc[nb][tb][2 * p], acc[nb][tb][2 * p + 1]);
+                }
+                (h ? Y : X)[0] = pk[0];
+                (h ? Y : X)[1] = pk[1];
+            }
+            // By rows, X = [x0 x1 x2 x3] and Y = [y0 y1 y2 y3] (x_q: d 4q..4q+3 of
+            // block 2nbp).  Swapping the halves gives [x0 x1 y0 y1], [x2 x3 y2 y3];
+            // swapping odd rows of the first with even rows of the second gives
+            // [x0 x2 y0 y2], [x1 x3 y1 y3]: row q holds 8 consecutive values of
+            // block 2nbp + q/2 at offset 8(q%2), in X then Y.
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const auto r0 = __builtin_amdgcn_permlane32_swap(X[i], Y[i], false, false);
+                const auto r1 = __builtin_amdgcn_permlane16_swap(r0[0], r0[1], false, false);
+                X[i] = r1[0];
+                Y[i] = r1[1];
+            }
+            if (live) stg16(drow + (2 * nbp + (q >> 1)) * 16 + (q & 1) * 8, make_uint4(X[0], X[1], Y[0], Y[1]));
+        }
+    }
+}
+
 // The occupancy is fixed by the LDS (one block per CU); saying so keeps the
 // scheduler from trading latency hiding for an occupancy it cannot reach.
 template <int DT>
@@ -388,20 +507,20 @@ void proj_kernel(ProjArgs a) {
         else dma16(xq + offB[u - kInstA] + k0, sb + wB + (u - kInstA) * 64 * 16);
     };
 
-    f32x16_t acc[4][kTB];
+    accv_t acc[kNB][kTB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
         for (int tb = 0; tb < kTB; ++tb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
+            for (int i = 0; i < kMf * kMf / 64; ++i) acc[nb][tb][i] = 0.f;
 
     const uint32_t KT = a.K / kProjTileK;              // >= 1: the host requires K % 64 == 0, K > 0
     constexpr int kPer = kInstA + kInstB;              // this wave's load instructions per stage
 #pragma unroll
     for (int u = 0; u < kPer; ++u) load_one(0, 0, u);
-    const int fr = lane & 31;          // fragment row (A) / column (B) of this lane
-    const int fk = lane >> 5;          // which 8-wide half of a 16-wide K step
+    const int fr = lane % kMf;         // fragment row (A) / column (B) of this lane
+    const int fk = lane / kMf;         // which 8-wide part of a K step
     // Main loop, in a fixed instruction order.  Each K step issues its
     // products one by one, with one fragment read of the next K step after
     // each of the first 4+kTB products and this wave's loads of the next
@@ -413,21 +532,21 @@ void proj_kernel(ProjArgs a) {
     // bounds), and the epilogue waits for those before it reuses the ring.
     // (Left to the compiler, the reads of a step were issued after most of
     // the products that could cover them.)
-    constexpr int KS = kProjTileK / 16;
-    constexpr int kM = 4 * kTB;                                   // products per K step
-    constexpr int kR = 4 + kTB;                                   // fragment reads per K step
+    constexpr int KS = kProjTileK / kKStep;
+    constexpr int kM = kNB * kTB;                                 // products per K step
+    constexpr int kR = kNB + kTB;                                 // fragment reads per K step
     constexpr int kLoadKs = ULY_PROJ_LOAD_KS < KS - 1 ? ULY_PROJ_LOAD_KS : KS - 1;
     constexpr int kLPer = (kPer + kLoadKs - 1) / kLoadKs;         // loads per loading step
     static_assert(kR <= kM && kLPer <= kM, "schedule shape");
-    auto read_frag = [&](const uint4 *sa, const uint4 *sb, int ks, int r, uint4 (&fa)[4], uint4 (&fb)[kTB]) {
-        const int c = ks * 2 + fk;
-        if (r < 4) fa[r] = sa[swz(wn * kProjD + r * 32 + fr, c)];
-        else fb[r - 4] = sb[swz(wt * kWaveT + (r - 4) * 32 + fr, c)];
+    auto read_frag = [&](const uint4 *sa, const uint4 *sb, int ks, int r, uint4 (&fa)[kNB], uint4 (&fb)[kTB]) {
+        const int c = ks * (kKStep / 8) + fk;
+        if (r < kNB) fa[r] = sa[swz(wn * kProjD + r * kMf + fr, c)];
+        else fb[r - kNB] = sb[swz(wt * kWaveT + (r - kNB) * kMf + fr, c)];
     };
 #define ULY_SB() __builtin_amdgcn_sched_barrier(0)
     // Products of (fa, fb); reads of K step `rks` (if >= 0) into (na, nb);
     // loads lbase .. lbase+lcount-1 of stage kn into slot sn.
-    auto kstep = [&](const uint4 (&fa)[4], const uint4 (&fb)[kTB], uint4 (&na)[4], uint4 (&nb)[kTB],
+    auto kstep = [&](const uint4 (&fa)[kNB], const uint4 (&fb)[kTB], uint4 (&na)[kNB], uint4 (&nb)[kTB],
                      const uint4 *sa, const uint4 *sb, int rks, int lbase, int lcount, uint32_t kn, uint32_t sn) {
 #pragma unroll
         for (int i = 0; i < kM; ++i) {
@@ -446,7 +565,7 @@ void proj_kernel(ProjArgs a) {
             }
         }
     };
-    uint4 fa[4], fb[kTB], ga[4], gb[kTB];
+    uint4 fa[kNB], fb[kTB], ga[kNB], gb[kTB];
     for (uint32_t kt = 0; kt < KT; ++kt) {
         const uint32_t st = kt % kStages;
         wait_vmcnt<0>();
@@ -478,7 +597,7 @@ void proj_kernel(ProjArgs a) {
         // keep it in (fa, fb) for the carry
         if ((KS & 1) == 1) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = ga[i];
+            for (int i = 0; i < kNB; ++i) fa[i] = ga[i];
 #pragma unroll
             for (int i = 0; i < kTB; ++i) fb[i] = gb[i];
         }
@@ -496,8 +615,13 @@ void proj_kernel(ProjArgs a) {
         lds_barrier();
     }
     const uint32_t hd = head0 + wn;
-    if (hd < a.Hq + a.Hkv) proj_epilogue<DT, true>(a, acc, m0, hd, wt, lane, tbl);
-    else if (hd < a.NH) proj_epilogue<DT, false>(a, acc, m0, hd, wt, lane, tbl);
+    if constexpr (kMf == 32) {
+        if (hd < a.Hq + a.Hkv) proj_epilogue<DT, true>(a, acc, m0, hd, wt, lane, tbl);
+        else if (hd < a.NH) proj_epilogue<DT, false>(a, acc, m0, hd, wt, lane, tbl);
+    } else {
+        if (hd < a.Hq + a.Hkv) proj_epilogue16<DT, true>(a, acc, m0, hd, wt, lane, tbl);
+        else if (hd < a.NH) proj_epilogue16<DT, false>(a, acc, m0, hd, wt, lane, tbl);
+    }
 }
 
 }  // namespace
