@@ -19,13 +19,13 @@ namespace uly {
 // kProjTileK at a time.
 // ---------------------------------------------------------------------------
 #ifndef ULY_PROJ_WAVE_T
-#define ULY_PROJ_WAVE_T 128
+#define ULY_PROJ_WAVE_T 64
 #endif
 constexpr int kProjD = 128;          // head dim the projection kernel is built for
 constexpr int kProjHeads = 2;        // heads per block, one per wave row
 constexpr int kProjTileT = 256;      // tokens per block
 constexpr int kProjWaveT = ULY_PROJ_WAVE_T;                            // tokens per wave
-constexpr int kProjThreads = kProjHeads * (kProjTileT / kProjWaveT) * 64;   // 4 waves (8 for 64)
+constexpr int kProjThreads = kProjHeads * (kProjTileT / kProjWaveT) * 64;   // 8 waves (4 for 128)
 #ifndef ULY_PROJ_TILE_K
 #define ULY_PROJ_TILE_K 64
 #endif

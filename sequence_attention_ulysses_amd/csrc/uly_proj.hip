@@ -5,22 +5,23 @@
 // output).
 //
 // The projection is the one dense contraction of the front end, so it runs
-// on the matrix cores: v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation.
-// The product is computed transposed, C^T[n][t] = sum_k W[n][k] X[t][k]:
-// both operands are K-contiguous rows, and the MFMA result then gives each
-// lane one token and 16 head-dim values (four runs of 4) per 32x32 block.
-// The RMSNorm of a (token, head) row is a sum over the lane's own registers
-// plus one exchange with lane ^ 32; the rotation pairs (2j, 2j+1) sit in
-// one lane's registers; one more exchange with lane ^ 32 turns the runs of 4
-// into 16-byte runs for the stores.
+// on the matrix cores: v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulation
+// (under this chip's power limit these reach ~15 % more products per second
+// on random data than v_mfma_f32_32x32x16, which also builds:
+// ULY_PROJ_MFMA=32).  The product is computed transposed,
+// C^T[n][t] = sum_k W[n][k] X[t][k]: both operands are K-contiguous rows,
+// and the MFMA result gives each lane one token and a run of 4 head-dim
+// values per 16x16 block.  The rotation pairs (2j, 2j+1) sit in one lane's
+// registers; the RMSNorm of a (token, head) row is a sum over the lane's
+// registers and over the token's four lane rows; exchanges across rows turn
+// the runs of 4 into 16-byte stores, 64 bytes per token per instruction.
 //
-// Tiling: a block of 4 waves owns two heads (256 output columns; each head
+// Tiling: a block of 8 waves owns two heads (256 output columns; each head
 // is one component q, k or v) and 256 tokens.  Wave (wn, wt) owns head wn
-// and tokens [128wt, 128wt+128): a 128 x 128 tile of 4 x 4 MFMA blocks, 256
-// fp32 accumulators per lane (in the accumulation registers), one wave per
-// SIMD.  Per product it reads 2/3 of the LDS bytes that 8 waves of 128 x 64
-// (two per SIMD) read; those let one wave's epilogue overlap the other's
-// products but measured ~2 % slower.  Both shapes build (ULY_PROJ_WAVE_T).
+// and tokens [64wt, 64wt+64): a 128 x 64 tile of 8 x 4 MFMA blocks, 128
+// fp32 accumulators per lane, two waves per SIMD.  (4 waves of 128 x 128,
+// one per SIMD, read 2/3 of the LDS bytes per product but measured ~2 %
+// slower with these products; ULY_PROJ_WAVE_T=128 builds them.)
 //
 // Operands go global -> LDS with global_load_lds_dwordx4 (no staging
 // registers, no ds_write) into a two-stage ring of 64-wide K stages; the
@@ -129,7 +130,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 #define ULY_PROJ_GROUP 4
 #endif
 #ifndef ULY_PROJ_LOAD_KS
-#define ULY_PROJ_LOAD_KS 3
+#define ULY_PROJ_LOAD_KS 1
 #endif
 
 // Block -> (token tile, head block).  Workgroups go to the 8 XCDs round
@@ -253,11 +254,12 @@ __device__ __forceinline__ float sum_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The epilogue of wave (wn, wt): RMSNorm + RoPE of q/k rows (QK), or v as
-// is, one rounding, and the stores into the head-sharded targets.  The head
-// (and so QK) is wave-uniform: each wave runs one straight-line body.
-// acc[nb][tb][i] is column n = 32nb + 8(i/4) + 4*half + i%4 (the head-dim
-// index d) of token m0 + kWaveT*wt + 32tb + lane%32 and head `hd`.
+// The epilogue of wave (wn, wt) for 32 x 32 blocks (ULY_PROJ_MFMA=32):
+// RMSNorm + RoPE of q/k rows (QK), or v as is, one rounding, and the stores
+// into the head-sharded targets.  The head (and so QK) is wave-uniform: each
+// wave runs one straight-line body.  acc[nb][tb][i] is column
+// n = 32nb + 8(i/4) + 4*half + i%4 (the head-dim index d) of token
+// m0 + kWaveT*wt + 32tb + lane%32 and head `hd`.
 template <int DT, bool QK>
 __device__ __forceinline__ void proj_epilogue(const ProjArgs &a, accv_t (&acc)[kNB][kTB], uint32_t m0,
                                               uint32_t hd, int wt, int lane, const float4 *tbl) {
@@ -535,7 +537,7 @@ void proj_kernel(ProjArgs a) {
     constexpr int KS = kProjTileK / kKStep;
     constexpr int kM = kNB * kTB;                                 // products per K step
     constexpr int kR = kNB + kTB;                                 // fragment reads per K step
-    constexpr int kLoadKs = ULY_PROJ_LOAD_KS < KS - 1 ? ULY_PROJ_LOAD_KS : KS - 1;
+    constexpr int kLoadKs = ULY_PROJ_LOAD_KS < KS ? ULY_PROJ_LOAD_KS : KS;
     constexpr int kLPer = (kPer + kLoadKs - 1) / kLoadKs;         // loads per loading step
     static_assert(kR <= kM && kLPer <= kM, "schedule shape");
     auto read_frag = [&](const uint4 *sa, const uint4 *sb, int ks, int r, uint4 (&fa)[kNB], uint4 (&fb)[kTB]) {
