@@ -272,53 +272,64 @@ def setup_spatial(torch, dev, synth, rope_table_1d, UlyssesContext):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def setup_video_dit_proj(torch, dev, synth, rope_table_1d, UlyssesContext):
+def _setup_proj(torch, dev, synth, rope_table_1d, UlyssesContext, w, seed, name):
     """The attention front end with the QKV projection fused in: one launch
     projects x, normalises and rotates q/k and stores every head band into
     its head-sharded target (flashinfer PR #6332's fused call), then the wait
     and the output gather.  Timed beside it: the per-operator path, a library
     GEMM (torch, hipBLASLt) writing qkv, then the fused norm/RoPE scatter."""
     import torch.nn.functional as F
-    w = synth.VIDEO_DIT
-    P, B, S_l, H, D = w.P, w.B, w.S_l, w.Hq, w.D
-    hidden, N = H * D, 3 * H * D
+    P, B, S_l, Hq, Hkv, D = w.P, w.B, w.S_l, w.Hq, w.Hkv, w.D
+    hidden, N = Hq * D, (Hq + 2 * Hkv) * D
     M = P * B * S_l
-    x = synth.normal((P, B, S_l, hidden), "bf16", 70, dev)
-    w_qkv = synth.normal((N, hidden), "bf16", 71, dev, std=hidden ** -0.5)
-    w_q, w_k = synth.norm_weight(D, "bf16", 72, dev), synth.norm_weight(D, "bf16", 73, dev)
+    x = synth.normal((P, B, S_l, hidden), "bf16", seed, dev)
+    w_qkv = synth.normal((N, hidden), "bf16", seed + 1, dev, std=hidden ** -0.5)
+    w_q, w_k = synth.norm_weight(D, "bf16", seed + 2, dev), synth.norm_weight(D, "bf16", seed + 3, dev)
     cos, sin = (t.to(dev) for t in rope_table_1d(P * S_l, D, theta=w.theta))
-    o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 74, dev)
+    o = synth.normal((P, B, P * S_l, Hq // P, D), "bf16", seed + 4, dev)
     ctx = UlyssesContext(P, device=0)
     flops = 2 * M * N * hidden
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    yv = y.view(P, B, S_l, 3, H, D)
+    y4 = y.view(P, B, S_l, N)
+    yq = y4[..., :Hq * D].unflatten(-1, (Hq, D))
+    yk = y4[..., Hq * D:(Hq + Hkv) * D].unflatten(-1, (Hkv, D))
+    yv = y4[..., (Hq + Hkv) * D:].unflatten(-1, (Hkv, D))
     x2 = x.view(M, hidden)
 
     def step():
-        ctx.fused_qkv_proj_norm_rope_scatter(x, w_qkv, H, H, w_q, w_k, cos, sin, eps=w.eps)
+        ctx.fused_qkv_proj_norm_rope_scatter(x, w_qkv, Hq, Hkv, w_q, w_k, cos, sin, eps=w.eps)
         ctx.wait()
         ctx.gather_out(o)
 
     def step_per_operator():
         F.linear(x2, w_qkv, out=y)
-        ctx.fused_qk_norm_rope_scatter(yv[:, :, :, 0], yv[:, :, :, 1], w_q, w_k, cos, sin, eps=w.eps,
-                                       v=yv[:, :, :, 2], tags=("pq", "pk", "pv"))
+        ctx.fused_qk_norm_rope_scatter(yq, yk, w_q, w_k, cos, sin, eps=w.eps, v=yv, tags=("pq", "pk", "pv"))
         ctx.wait()
         ctx.gather_out(o)
 
-    return {"workload": w, "name": "video_dit_proj_p4_s16384_h24_hidden3072_bf16", "ctx": ctx, "step": step,
+    return {"workload": w, "name": name, "ctx": ctx, "step": step,
             "step_per_operator": step_per_operator,
             "bytes_per_step": flops, "unit": "TFLOP/s", "unit_div": 1e12,
             "metric": "QKV projection + QK-norm + RoPE + Ulysses scatter + output gather, projection TFLOP/s "
-                      "over the step, P=4 bf16, 1 MI355X",
+                      "over the step, P=%d bf16, 1 MI355X" % P,
             "dominant": ("proj", flops, "proj_kernel<bf16> (MFMA QKV projection with norm/RoPE/band-store "
                          "epilogue)", "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"),
-            "cpu_proj": (x, w_qkv, w_q, w_k, H, w.eps, w.theta),
+            "cpu_proj": (x, w_qkv, w_q, w_k, Hq, Hkv, w.eps, w.theta),
             "dtype": "bf16", "data": "synthetic N(0,1) activations, N(0,1/hidden) QKV weight, N(1,0.1) norm "
                                      "weights, 1-D RoPE theta 1e4 (seeded)",
-            "config": {"workload": "video_dit_proj_p4_s16384_h24_hidden3072_bf16", "P": P, "B": B, "S_local": S_l,
-                       "S": P * S_l, "H": H, "D": D, "hidden": hidden, "M": M, "N": N,
-                       "flops_per_step": flops, "parallelism": "ulysses-p4-emulated"}}
+            "config": {"workload": name, "P": P, "B": B, "S_local": S_l, "S": P * S_l, "Hq": Hq, "Hkv": Hkv,
+                       "D": D, "hidden": hidden, "M": M, "N": N, "flops_per_step": flops,
+                       "parallelism": "ulysses-p%d-emulated" % P}}
+
+
+def setup_video_dit_proj(torch, dev, synth, rope_table_1d, UlyssesContext):
+    return _setup_proj(torch, dev, synth, rope_table_1d, UlyssesContext, synth.VIDEO_DIT, 70,
+                       "video_dit_proj_p4_s16384_h24_hidden3072_bf16")
+
+
+def setup_gqa_proj(torch, dev, synth, rope_table_1d, UlyssesContext):
+    return _setup_proj(torch, dev, synth, rope_table_1d, UlyssesContext, synth.GQA, 80,
+                       "gqa_proj_p8_b2_s65536_hq32_hkv8_hidden4096_bf16")
 
 
 def cpu_baseline_proj(args, proj_inputs, min_seconds: float = 10.0):
@@ -330,7 +341,7 @@ def cpu_baseline_proj(args, proj_inputs, min_seconds: float = 10.0):
     from oracle import oracle
     from sequence_attention_ulysses_amd import synth
 
-    x, w_qkv, w_q, w_k, H, eps, theta = proj_inputs
+    x, w_qkv, w_q, w_k, Hq, Hkv, eps, theta = proj_inputs
     P, B, S_l, hidden = x.shape
     D = w_q.numel()
     xb, wb = synth.bits(x.cpu()).reshape(-1, hidden), synth.bits(w_qkv.cpu())
@@ -342,7 +353,7 @@ def cpu_baseline_proj(args, proj_inputs, min_seconds: float = 10.0):
         rows = rng.integers(0, xb.shape[0], size=n)
         pos = (rows // (B * S_l)) * S_l + rows % S_l
         t0 = time.perf_counter()
-        oracle.qkv_proj_norm_rope_rows(xb[rows], "bf16", wb, H, H, D, wqb, wkb, eps, cos, sin, pos)
+        oracle.qkv_proj_norm_rope_rows(xb[rows], "bf16", wb, Hq, Hkv, D, wqb, wkb, eps, cos, sin, pos)
         dt += time.perf_counter() - t0
         reps += 1
     flops = 2.0 * reps * n * wb.shape[0] * hidden
@@ -353,7 +364,7 @@ def cpu_baseline_proj(args, proj_inputs, min_seconds: float = 10.0):
 
 
 WORKLOADS = {"video_dit": setup_video_dit, "wan_long": setup_wan_long, "gqa": setup_gqa, "tiny": setup_tiny,
-             "spatial": setup_spatial, "video_dit_proj": setup_video_dit_proj}
+             "spatial": setup_spatial, "video_dit_proj": setup_video_dit_proj, "gqa_proj": setup_gqa_proj}
 
 
 def measure_protocol(args, torch, dev, setup, step, timed, samples: int = 100):

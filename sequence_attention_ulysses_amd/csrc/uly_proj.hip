@@ -72,7 +72,11 @@ constexpr int kWavesPerSimd = kWaves / 4;                // occupancy: one block
 static_assert(kChunks == 4 || kChunks == 8, "LDS rows of 64 or 128 bytes");
 static_assert(kWaves == kProjHeads * kWavesT && (kWaveT == 64 || kWaveT == 128), "wave grid");
 
-constexpr int kStages = 2;                               // LDS ring: the stage in use and the next
+#ifndef ULY_PROJ_STAGES
+#define ULY_PROJ_STAGES 2
+#endif
+constexpr int kStages = ULY_PROJ_STAGES;                 // LDS ring: the stage in use and kStages-1 ahead
+static_assert(kStages >= 2, "a ring of at least two stages");
 constexpr int kSlotsA = kRowsA * kChunks, kSlotsB = kRowsB * kChunks;   // 16-byte slots per stage
 constexpr int kInstA = kSlotsA / 64 / kWaves, kInstB = kSlotsB / 64 / kWaves;   // loads per wave per stage
 static_assert(kSlotsA % (64 * kWaves) == 0 && kSlotsB % (64 * kWaves) == 0, "whole wave instructions");
@@ -520,7 +524,9 @@ void proj_kernel(ProjArgs a) {
     const uint32_t KT = a.K / kProjTileK;              // >= 1: the host requires K % 64 == 0, K > 0
     constexpr int kPer = kInstA + kInstB;              // this wave's load instructions per stage
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) load_one(0, 0, u);
+    for (int p = 0; p + 1 < kStages; ++p)
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) load_one(min(uint32_t(p), KT - 1), p, u);
     const int fr = lane % kMf;         // fragment row (A) / column (B) of this lane
     const int fk = lane / kMf;         // which 8-wide part of a K step
     // Main loop, in a fixed instruction order.  Each K step issues its
@@ -570,9 +576,9 @@ void proj_kernel(ProjArgs a) {
     uint4 fa[kNB], fb[kTB], ga[kNB], gb[kTB];
     for (uint32_t kt = 0; kt < KT; ++kt) {
         const uint32_t st = kt % kStages;
-        wait_vmcnt<0>();
+        wait_vmcnt<(kStages - 2) * kPer>();   // this stage's loads landed; later stages may be in flight
         lds_barrier();
-        const uint32_t kn = min(kt + 1, KT - 1), sn = (kt + 1) % kStages;
+        const uint32_t kn = min(kt + kStages - 1, KT - 1), sn = (kt + kStages - 1) % kStages;
         const uint4 *sa = lds + st * (kSlotsA + kSlotsB), *sb = sa + kSlotsA;
         // multiply steps of this iteration: m = 0 is the carried last step of
         // the previous stage (none at kt = 0, where step 0 is read first)
