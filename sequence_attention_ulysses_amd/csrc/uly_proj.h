@@ -48,6 +48,8 @@ struct ProjArgs {
     float eps, inv_D;
 };
 
-void launch_proj(const ProjArgs &a, int dtype, uint32_t blocks, hipStream_t stream);
+// deep_b: three-stage ring for the token rows (a token operand too large to
+// stay in the caches), else two.
+void launch_proj(const ProjArgs &a, int dtype, uint32_t blocks, bool deep_b, hipStream_t stream);
 
 }  // namespace uly

@@ -72,11 +72,12 @@ constexpr int kWavesPerSimd = kWaves / 4;                // occupancy: one block
 static_assert(kChunks == 4 || kChunks == 8, "LDS rows of 64 or 128 bytes");
 static_assert(kWaves == kProjHeads * kWavesT && (kWaveT == 64 || kWaveT == 128), "wave grid");
 
-#ifndef ULY_PROJ_STAGES
-#define ULY_PROJ_STAGES 2
-#endif
-constexpr int kStages = ULY_PROJ_STAGES;                 // LDS ring: the stage in use and kStages-1 ahead
-static_assert(kStages >= 2, "a ring of at least two stages");
+// LDS rings: the weight rows (A) and the token rows (B) of a K stage each
+// have their own ring, the stage in use plus depth-1 stages ahead.  A is
+// two deep; B is two deep when the token operand stays in the caches and
+// three deep (the kernel's BD parameter) when it streams from HBM: the
+// weights are shared by every token tile and stay cached.
+constexpr int kDepthA = 2;
 constexpr int kSlotsA = kRowsA * kChunks, kSlotsB = kRowsB * kChunks;   // 16-byte slots per stage
 constexpr int kInstA = kSlotsA / 64 / kWaves, kInstB = kSlotsB / 64 / kWaves;   // loads per wave per stage
 static_assert(kSlotsA % (64 * kWaves) == 0 && kSlotsB % (64 * kWaves) == 0, "whole wave instructions");
@@ -85,10 +86,10 @@ static_assert(kSlotsA % (64 * kWaves) == 0 && kSlotsB % (64 * kWaves) == 0, "who
 // chunk of padding so that 16 lanes reading the same chunk of 16 different
 // rows start 4 banks apart and cover the 64 banks once.
 constexpr int kTblRow = kProjD / 4 + 1;                  // 16-byte chunks per token row
-constexpr int kRingSlots = kStages * (kSlotsA + kSlotsB);
+constexpr int ring_slots(int depth_b) { return kDepthA * kSlotsA + depth_b * kSlotsB; }
 constexpr int kTblSlots = kProjTileT * kTblRow;
-constexpr int kLdsSlots = kRingSlots > kTblSlots ? kRingSlots : kTblSlots;
-static_assert(kLdsSlots * 16 <= 160 * 1024, "LDS of one workgroup");
+constexpr int lds_slots(int depth_b) { return ring_slots(depth_b) > kTblSlots ? ring_slots(depth_b) : kTblSlots; }
+static_assert(lds_slots(3) * 16 <= 160 * 1024, "LDS of one workgroup");
 
 #ifndef ULY_PROJ_NT_STORE
 #define ULY_PROJ_NT_STORE 0
@@ -464,10 +465,12 @@ __device__ __forceinline__ void proj_epilogue16(const ProjArgs &a, accv_t (&acc)
 
 // The occupancy is fixed by the LDS (one block per CU); saying so keeps the
 // scheduler from trading latency hiding for an occupancy it cannot reach.
-template <int DT>
+template <int DT, int BD>
 __global__ __launch_bounds__(kProjThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 void proj_kernel(ProjArgs a) {
-    __shared__ uint4 lds[kLdsSlots];
+    constexpr int kDepthB = BD;
+    static_assert(kDepthB >= kDepthA, "B at least as deep as A");
+    __shared__ uint4 lds[lds_slots(kDepthB)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -504,13 +507,13 @@ void proj_kernel(ProjArgs a) {
     const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)(&lds[0]));
     const uint32_t wu = __builtin_amdgcn_readfirstlane(uint32_t(wv));
     const uint32_t wA = wu * kInstA * 64 * 16;
-    const uint32_t wB = kSlotsA * 16 + wu * kInstB * 64 * 16;
-    // Load instruction u (A rows first, then B rows) of stage kt into ring slot st.
-    auto load_one = [&](uint32_t kt, uint32_t st, int u) {
-        const uint32_t k0 = kt * (kProjTileK / 8);
-        const uint32_t sb = ring + st * (kSlotsA + kSlotsB) * 16;
-        if (u < kInstA) dma16(wq + offA[u] + k0, sb + wA + u * 64 * 16);
-        else dma16(xq + offB[u - kInstA] + k0, sb + wB + (u - kInstA) * 64 * 16);
+    const uint32_t wB = kDepthA * kSlotsA * 16 + wu * kInstB * 64 * 16;
+    // Load instruction u: A rows (u < kInstA) of stage ka into A slot sa, or
+    // B rows of stage kb into B slot sb.
+    auto load_one = [&](int u, uint32_t ka, uint32_t sa, uint32_t kb, uint32_t sb) {
+        if (u < kInstA) dma16(wq + offA[u] + ka * (kProjTileK / 8), ring + sa * kSlotsA * 16 + wA + u * 64 * 16);
+        else dma16(xq + offB[u - kInstA] + kb * (kProjTileK / 8),
+                   ring + sb * kSlotsB * 16 + wB + (u - kInstA) * 64 * 16);
     };
 
     accv_t acc[kNB][kTB];
@@ -523,10 +526,22 @@ void proj_kernel(ProjArgs a) {
 
     const uint32_t KT = a.K / kProjTileK;              // >= 1: the host requires K % 64 == 0, K > 0
     constexpr int kPer = kInstA + kInstB;              // this wave's load instructions per stage
+    // the stages ahead of the first: A's, then B's (the waits below count on this order)
 #pragma unroll
-    for (int p = 0; p + 1 < kStages; ++p)
+    for (int p = 0; p + 1 < kDepthA; ++p)
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) load_one(min(uint32_t(p), KT - 1), p, u);
+        for (int u = 0; u < kInstA; ++u) load_one(u, min(uint32_t(p), KT - 1), p, 0, 0);
+#pragma unroll
+    for (int p = 0; p + 1 < kDepthB; ++p)
+#pragma unroll
+        for (int u = kInstA; u < kPer; ++u) load_one(u, 0, 0, min(uint32_t(p), KT - 1), p);
+    // At the top of stage kt its A and B loads must have landed.  Every
+    // iteration issues its A loads (stage + kDepthA - 1) before its B loads
+    // (stage + kDepthB - 1), so the loads still allowed in flight are the
+    // later iterations' ones: after B(kt), (kDepthB - 2) iterations' worth;
+    // after A(kt), its own iteration's B loads and (kDepthA - 2) iterations'.
+    constexpr int kWaitB = (kDepthB - 2) * kPer, kWaitA = kInstB + (kDepthA - 2) * kPer;
+    constexpr int kWait = kWaitB < kWaitA ? kWaitB : kWaitA;
     const int fr = lane % kMf;         // fragment row (A) / column (B) of this lane
     const int fk = lane / kMf;         // which 8-wide part of a K step
     // Main loop, in a fixed instruction order.  Each K step issues its
@@ -553,9 +568,11 @@ void proj_kernel(ProjArgs a) {
     };
 #define ULY_SB() __builtin_amdgcn_sched_barrier(0)
     // Products of (fa, fb); reads of K step `rks` (if >= 0) into (na, nb);
-    // loads lbase .. lbase+lcount-1 of stage kn into slot sn.
+    // loads lbase .. lbase+lcount-1 (A of stage ka into A slot za, B of
+    // stage kb into B slot zb).
     auto kstep = [&](const uint4 (&fa)[kNB], const uint4 (&fb)[kTB], uint4 (&na)[kNB], uint4 (&nb)[kTB],
-                     const uint4 *sa, const uint4 *sb, int rks, int lbase, int lcount, uint32_t kn, uint32_t sn) {
+                     const uint4 *sa, const uint4 *sb, int rks, int lbase, int lcount, uint32_t ka, uint32_t za,
+                     uint32_t kb, uint32_t zb) {
 #pragma unroll
         for (int i = 0; i < kM; ++i) {
             acc[i / kTB][i % kTB] = mfma<DT>(fa[i / kTB], fb[i % kTB], acc[i / kTB][i % kTB]);
@@ -567,7 +584,7 @@ void proj_kernel(ProjArgs a) {
             if (lcount > 0) {
                 const int l0 = (i * lcount) / kM, l1 = ((i + 1) * lcount) / kM;
                 if (l1 != l0) {
-                    load_one(kn, sn, lbase + l0);
+                    load_one(lbase + l0, ka, za, kb, zb);
                     ULY_SB();
                 }
             }
@@ -575,11 +592,11 @@ void proj_kernel(ProjArgs a) {
     };
     uint4 fa[kNB], fb[kTB], ga[kNB], gb[kTB];
     for (uint32_t kt = 0; kt < KT; ++kt) {
-        const uint32_t st = kt % kStages;
-        wait_vmcnt<(kStages - 2) * kPer>();   // this stage's loads landed; later stages may be in flight
+        wait_vmcnt<kWait>();
         lds_barrier();
-        const uint32_t kn = min(kt + kStages - 1, KT - 1), sn = (kt + kStages - 1) % kStages;
-        const uint4 *sa = lds + st * (kSlotsA + kSlotsB), *sb = sa + kSlotsA;
+        const uint32_t ka = min(kt + kDepthA - 1, KT - 1), za = (kt + kDepthA - 1) % kDepthA;
+        const uint32_t kb = min(kt + kDepthB - 1, KT - 1), zb = (kt + kDepthB - 1) % kDepthB;
+        const uint4 *sa = lds + (kt % kDepthA) * kSlotsA, *sb = lds + kDepthA * kSlotsA + (kt % kDepthB) * kSlotsB;
         // multiply steps of this iteration: m = 0 is the carried last step of
         // the previous stage (none at kt = 0, where step 0 is read first)
 #pragma unroll
@@ -594,12 +611,12 @@ void proj_kernel(ProjArgs a) {
 #pragma unroll
                 for (int r = 0; r < kR; ++r) read_frag(sa, sb, 0, r, ga, gb);
 #pragma unroll
-                for (int l = 0; l < lc; ++l) load_one(kn, sn, lb + l);
+                for (int l = 0; l < lc; ++l) load_one(lb + l, ka, za, kb, zb);
                 ULY_SB();
                 continue;
             }
-            if ((m & 1) == 0) kstep(fa, fb, ga, gb, sa, sb, m, lb, lc, kn, sn);
-            else kstep(ga, gb, fa, fb, sa, sb, m, lb, lc, kn, sn);
+            if ((m & 1) == 0) kstep(fa, fb, ga, gb, sa, sb, m, lb, lc, ka, za, kb, zb);
+            else kstep(ga, gb, fa, fb, sa, sb, m, lb, lc, ka, za, kb, zb);
         }
         // step KS-1 read into (fa, fb) if KS-1 is odd, else into (ga, gb):
         // keep it in (fa, fb) for the carry
@@ -610,7 +627,7 @@ void proj_kernel(ProjArgs a) {
             for (int i = 0; i < kTB; ++i) fb[i] = gb[i];
         }
     }
-    if (KT > 0) kstep(fa, fb, ga, gb, nullptr, nullptr, -1, 0, 0, 0, 0);
+    if (KT > 0) kstep(fa, fb, ga, gb, nullptr, nullptr, -1, 0, 0, 0, 0, 0, 0);
 #undef ULY_SB
     wait_vmcnt<0>();      // the last stage's repeat loads land before the ring is reused
 
@@ -634,11 +651,14 @@ void proj_kernel(ProjArgs a) {
 
 }  // namespace
 
-void launch_proj(const ProjArgs &a, int dtype, uint32_t blocks, hipStream_t stream) {
-    if (dtype == ULY_BF16)
-        hipLaunchKernelGGL(proj_kernel<2>, dim3(blocks), dim3(kProjThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(proj_kernel<1>, dim3(blocks), dim3(kProjThreads), 0, stream, a);
+void launch_proj(const ProjArgs &a, int dtype, uint32_t blocks, bool deep_b, hipStream_t stream) {
+    if (dtype == ULY_BF16) {
+        if (deep_b) hipLaunchKernelGGL((proj_kernel<2, 3>), dim3(blocks), dim3(kProjThreads), 0, stream, a);
+        else hipLaunchKernelGGL((proj_kernel<2, 2>), dim3(blocks), dim3(kProjThreads), 0, stream, a);
+    } else {
+        if (deep_b) hipLaunchKernelGGL((proj_kernel<1, 3>), dim3(blocks), dim3(kProjThreads), 0, stream, a);
+        else hipLaunchKernelGGL((proj_kernel<1, 2>), dim3(blocks), dim3(kProjThreads), 0, stream, a);
+    }
 }
 
 }  // namespace uly

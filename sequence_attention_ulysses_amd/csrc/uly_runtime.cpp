@@ -869,7 +869,10 @@ uly_status fused_qkv_proj_norm_rope_scatter(uly_ctx *c, const void *x, int dtype
     const uint32_t blocks = uint32_t(tiles * NHB);
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
-    if ((st = launch(c, ULY_K_PROJ, caller, [&] { launch_proj(a, dtype, blocks, caller); })) != ULY_OK) return st;
+    // a token operand beyond the Infinity Cache streams from HBM: prefetch its rows deeper
+    const bool deep_b = M * hidden * 2 > kCacheResidentBytes;
+    if ((st = launch(c, ULY_K_PROJ, caller, [&] { launch_proj(a, dtype, blocks, deep_b, caller); })) != ULY_OK)
+        return st;
     return mark_pending(c, caller);
 }
 
