@@ -363,6 +363,13 @@ uly_status uly_set_route(uly_ctx *ctx, int route);
  * launch (0 = the next one) is not enqueued and reports a HIP failure. */
 uly_status uly_debug_fail_launch(uly_ctx *ctx, int after);
 
+/* Test hook: the depth of fused_qkv_proj_norm_rope_scatter's LDS ring for
+ * the token rows.  0 (the default) picks three stages when the token
+ * operand exceeds the 256 MB Infinity Cache and two otherwise; 2 or 3
+ * force that depth, so that both kernels can be checked at any size.
+ * Other values: ULY_E_INVAL. */
+uly_status uly_debug_proj_ring(uly_ctx *ctx, int depth);
+
 const char *uly_last_error(void);
 const char *uly_status_string(int status);
 

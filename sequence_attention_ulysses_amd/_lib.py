@@ -49,8 +49,8 @@ EXPORTS = (
     "uly_seq_pad_shard", "uly_seq_unshard_trim", "uly_spatial_split_halo",
     "uly_spatial_gather_stacked", "uly_spatial_trim_concat", "uly_rope_table_1d",
     "uly_rope_table_3d", "uly_profile_enable", "uly_profile_read", "uly_profile_reset",
-    "uly_get_stats", "uly_comm_stream", "uly_set_route", "uly_debug_fail_launch", "uly_last_error",
-    "uly_status_string",
+    "uly_get_stats", "uly_comm_stream", "uly_set_route", "uly_debug_fail_launch", "uly_debug_proj_ring",
+    "uly_last_error", "uly_status_string",
 )
 
 
@@ -160,6 +160,7 @@ def load() -> ctypes.CDLL:
         "uly_comm_stream": [vp, ctypes.POINTER(vp)],
         "uly_set_route": [vp, i32],
         "uly_debug_fail_launch": [vp, i32],
+        "uly_debug_proj_ring": [vp, i32],
     }
     for name, argtypes in sig.items():
         fn = getattr(lib, name)

@@ -491,3 +491,7 @@ class UlyssesContext:
 
     def debug_fail_launch(self, after: int = 0) -> None:
         check(self._lib.uly_debug_fail_launch(self._h(), int(after)), "uly_debug_fail_launch")
+
+    def debug_proj_ring(self, depth: int = 0) -> None:
+        """Test hook: force the projection's token-row ring depth (2 or 3), or 0 for automatic."""
+        check(self._lib.uly_debug_proj_ring(self._h(), int(depth)), "uly_debug_proj_ring")

@@ -174,6 +174,7 @@ struct uly_ctx {
     uly_stats stats{};
     int fail_after = -1;
     int route = ULY_ROUTE_KERNEL;   // how ulysses_scatter_qkv moves its operands
+    int proj_ring = 0;              // token-row ring depth of the projection: 0 automatic, else 2 or 3
 };
 
 namespace {
@@ -870,7 +871,7 @@ uly_status fused_qkv_proj_norm_rope_scatter(uly_ctx *c, const void *x, int dtype
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
     // a token operand beyond the Infinity Cache streams from HBM: prefetch its rows deeper
-    const bool deep_b = M * hidden * 2 > kCacheResidentBytes;
+    const bool deep_b = c->proj_ring ? c->proj_ring == 3 : M * hidden * 2 > kCacheResidentBytes;
     if ((st = launch(c, ULY_K_PROJ, caller, [&] { launch_proj(a, dtype, blocks, deep_b, caller); })) != ULY_OK)
         return st;
     return mark_pending(c, caller);
@@ -1201,6 +1202,14 @@ uly_status uly_debug_fail_launch(uly_ctx *c, int after) {
     uly_status st = ctx_ok(c);
     if (st != ULY_OK) return st;
     c->fail_after = after < 0 ? -1 : after;
+    return ULY_OK;
+}
+
+uly_status uly_debug_proj_ring(uly_ctx *c, int depth) {
+    uly_status st = ctx_ok(c);
+    if (st != ULY_OK) return st;
+    if (depth != 0 && depth != 2 && depth != 3) return fail(ULY_E_INVAL, "ring depth %d: 0, 2 or 3", depth);
+    c->proj_ring = depth;
     return ULY_OK;
 }
 

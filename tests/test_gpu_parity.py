@@ -874,15 +874,19 @@ PROJ_SMALL = [
 ]
 
 
+@pytest.mark.parametrize("ring", [0, 3])
 @pytest.mark.parametrize("P,B,S_l,hidden,Hq,Hkv,dtype", PROJ_SMALL)
-def test_projection_small(dev, orc, P, B, S_l, hidden, Hq, Hkv, dtype):
+def test_projection_small(dev, orc, P, B, S_l, hidden, Hq, Hkv, dtype, ring):
     """flashinfer PR #6332, 'Description' / 'Assumptions': projection -> QK-norm -> RoPE ->
-    exchange, against the double-precision oracle element by element."""
+    exchange, against the double-precision oracle element by element.  ring=3 forces the
+    kernel with the three-stage token-row ring (chosen by itself only for operands beyond
+    the Infinity Cache)."""
     x, w, wq, wk = _proj_inputs(P, B, S_l, hidden, Hq, Hkv, dtype, 60, dev)
     rows = P * S_l + 3
     cos, sin = rope_table_1d(rows, 128)
     ocos, osin = orc.rope_table_1d(rows, 128)
     with UlyssesContext(P, device=0) as ctx:
+        ctx.debug_proj_ring(ring)
         yq, yk, yv = ctx.fused_qkv_proj_norm_rope_scatter(x, w, Hq, Hkv, wq, wk, cos.to(dev), sin.to(dev))
         ctx.wait()
         torch.cuda.synchronize()

@@ -483,6 +483,16 @@ def _proj(lib, c, B=1, S_l=16, hidden=256, Hq=8, Hkv=4, D=128, dtype=_lib.BF16, 
                                                 _lib.ptr_array(outs), None)
 
 
+def test_projection_ring_hook(lib, ctx4):
+    """The test hook that forces the projection's token-row ring depth takes 0, 2 or 3."""
+    for depth in (0, 2, 3, 0):
+        assert lib.uly_debug_proj_ring(ctx4.h, depth) == _lib.OK
+    for depth in (1, 4, -1):
+        assert lib.uly_debug_proj_ring(ctx4.h, depth) == _lib.E_INVAL
+        assert b"ring depth" in lib.uly_last_error()
+    assert lib.uly_debug_proj_ring(None, 0) == _lib.E_INVAL
+
+
 def test_projection_checks(lib, ctx4):
     """flashinfer PR #6332, 'Description' / 'Assumptions': BF16 operands, head_dim 128,
     heads divisible by the world size, rejected before any launch."""
