@@ -24,8 +24,10 @@
 // slower with these products; ULY_PROJ_WAVE_T=128 builds them.)
 //
 // Operands go global -> LDS with global_load_lds_dwordx4 (no staging
-// registers, no ds_write) into a two-stage ring of 64-wide K stages; the
-// next stage's loads are in flight while a stage is multiplied.  LDS rows are
+// registers, no ds_write) into rings of 64-wide K stages, two deep for the
+// weight rows and two or three deep for the token rows (three when they
+// stream from HBM); later stages' loads are in flight while a stage is
+// multiplied.  LDS rows are
 // XOR-swizzled so the 16-byte fragment reads do not collide on banks.  The
 // main loop's instruction order is fixed by hand (scheduling barriers): each
 // product is followed by at most one fragment read of the next K step and
@@ -546,13 +548,14 @@ void proj_kernel(ProjArgs a) {
     const int fk = lane / kMf;         // which 8-wide part of a K step
     // Main loop, in a fixed instruction order.  Each K step issues its
     // products one by one, with one fragment read of the next K step after
-    // each of the first 4+kTB products and this wave's loads of the next
-    // stage spread over the products of the first kLoadKs steps.  The last K
-    // step of a stage is read before the next barrier and multiplied after
-    // it, so its products cover the LDS reads that open the next stage, and
-    // the next stage's loads go out right after the barrier.  The loads are
-    // unconditional: the last stage loads itself again into the free slot (in
-    // bounds), and the epilogue waits for those before it reuses the ring.
+    // each of the first kNB+kTB products and this wave's loads of the stages
+    // ahead (A's, then B's) spread over the products of the first kLoadKs
+    // steps.  The last K step of a stage is read before the next barrier and
+    // multiplied after it, so its products cover the LDS reads that open the
+    // next stage, and the loads go out right after the barrier.  The loads
+    // are unconditional: past the last stage they load it again into a free
+    // slot (in bounds), and the epilogue waits for them before it reuses the
+    // rings.
     // (Left to the compiler, the reads of a step were issued after most of
     // the products that could cover them.)
     constexpr int KS = kProjTileK / kKStep;
