@@ -19,6 +19,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -45,6 +46,20 @@ uly_status fail(uly_status st, const char *fmt, ...) {
 constexpr int kMaxTargetsCap = 12;   // [P27 "Changes Made"]
 constexpr int kTagMax = 63;
 constexpr int64_t kMaxVecs = int64_t(1) << 31;   // per launch plan, keeps 32-bit indexing exact
+constexpr int kMaxWorld = 4096;                  // emulated ranks per context
+// Bound on any element count or byte size formed from caller extents (far
+// beyond any device's memory).  Sizes below it leave room for the further
+// products by P, the element size and 16 that the plans form, in int64.
+constexpr int64_t kMaxExtent = int64_t(1) << 48;
+
+// The product of non-negative factors, or -1 when a factor is negative or the
+// product passes kMaxExtent.  Checked factor by factor, so no product wraps.
+int64_t checked_prod(std::initializer_list<int64_t> f) {
+    int64_t r = 1;
+    for (int64_t v : f)
+        if (v < 0 || __builtin_mul_overflow(r, v, &r) || r > kMaxExtent) return -1;
+    return r;
+}
 
 struct Target {
     std::string tag;
@@ -102,6 +117,12 @@ uly_status check_operand(const uly_tensor *t, const char *name, int P, Operand &
     if (t->rank_stride < 0 || t->stride[0] < 0 || t->stride[1] < 0 || t->stride[2] < 0)
         return fail(ULY_E_INVAL, "%s: negative stride", name);
     const int64_t es = elem_size(t->dtype);
+    // Bounded extents and strides keep every size and offset formed below in int64.
+    if (checked_prod({P, t->shape[0], t->shape[1], t->shape[2], t->shape[3], es}) < 0 ||
+        checked_prod({P, t->shape[1]}) < 0 || checked_prod({t->shape[2], t->shape[3], es}) < 0 ||
+        t->shape[0] > kMaxExtent || t->rank_stride > kMaxExtent || t->stride[0] > kMaxExtent || t->stride[1] > kMaxExtent ||
+        t->stride[2] > kMaxExtent)
+        return fail(ULY_E_UNSUPPORTED, "%s: extents or strides too large", name);
     if ((t->shape[3] * es) % 16 != 0)
         return fail(ULY_E_INVAL, "%s: a head row of %lld bytes is not a multiple of 16", name,
                     (long long)(t->shape[3] * es));
@@ -126,7 +147,11 @@ uly_status check_operand(const uly_tensor *t, const char *name, int P, Operand &
         if (!o.data) return fail(ULY_E_INVAL, "%s: null data pointer", name);
         if (!aligned16(o.data)) return fail(ULY_E_INVAL, "%s: data pointer not 16-byte aligned", name);
         int64_t maxoff = o.D - 1;
-        for (int i = 0; i < 4; ++i) maxoff += (ext[i] - 1) * str[i];
+        for (int i = 0; i < 4; ++i) {
+            const int64_t span = checked_prod({ext[i] - 1, str[i], es});
+            if (span < 0) return fail(ULY_E_UNSUPPORTED, "%s: strides too large", name);
+            maxoff += span / es;      // at most 4 terms below 2^48: no wrap
+        }
         o.range.lo = reinterpret_cast<uintptr_t>(o.data);
         o.range.hi = o.range.lo + uintptr_t(maxoff + 1) * uintptr_t(es);
     }
@@ -447,7 +472,8 @@ const char *uly_status_string(int st) {
 uly_status uly_create(uly_ctx **out, int device, int world_size, int max_targets) {
     if (!out) return fail(ULY_E_INVAL, "null output pointer");
     *out = nullptr;
-    if (world_size < 1) return fail(ULY_E_INVAL, "world_size must be >= 1 (got %d)", world_size);
+    if (world_size < 1 || world_size > kMaxWorld)
+        return fail(ULY_E_INVAL, "world_size must be in [1, %d] (got %d)", kMaxWorld, world_size);
     if (max_targets < 1 || max_targets > kMaxTargetsCap)
         return fail(ULY_E_INVAL, "max_targets must be in [1, %d] (got %d)", kMaxTargetsCap, max_targets);
     if (device < -1) return fail(ULY_E_INVAL, "device must be >= -1 (got %d)", device);
@@ -687,6 +713,7 @@ static uly_status fused_scatter(uly_ctx *c, const uly_tensor *q, const uly_tenso
     if (table_rows < int64_t(c->P) * S)
         return fail(ULY_E_INVAL, "table has %lld rows, positions reach %lld", (long long)table_rows,
                     (long long)(int64_t(c->P) * S));
+    if (checked_prod({table_rows, D / 2, 4}) < 0) return fail(ULY_E_UNSUPPORTED, "table too large");
     for (int i = 0; i < 3; ++i) {
         if (!mem[i] || ops[i].empty()) continue;
         const Operand &x = ops[i];
@@ -706,6 +733,12 @@ static uly_status fused_scatter(uly_ctx *c, const uly_tensor *q, const uly_tenso
     if (w_q) in_ranges.push_back(byte_range(w_q, D * 2));
     if (w_k) in_ranges.push_back(byte_range(w_k, D * 2));
     if ((st = check_overlaps(in_ranges, out_ranges)) != ULY_OK) return st;
+
+    const int64_t Hall = (q ? ops[0].H : 0) + (k ? ops[1].H : 0) + (v ? ops[2].H : 0);
+    const int64_t tokens = int64_t(c->P) * B * S;
+    if (tokens >= kMaxVecs || checked_prod({tokens, Hall}) < 0 || tokens * Hall >= kMaxVecs)
+        return fail(ULY_E_UNSUPPORTED, "too many rows for one launch (%lld tokens x %lld heads)", (long long)tokens,
+                    (long long)Hall);
 
     NormRopeArgs a{};
     uint32_t Hrows[3] = {0, 0, 0};
@@ -736,9 +769,6 @@ static uly_status fused_scatter(uly_ctx *c, const uly_tensor *q, const uly_tenso
         Hrows[i] = uint32_t(x.H);
     }
     const uint32_t Hsum = Hrows[0] + Hrows[1] + Hrows[2];
-    const int64_t tokens = int64_t(c->P) * B * S;
-    if (tokens * Hsum >= kMaxVecs || tokens >= kMaxVecs)
-        return fail(ULY_E_UNSUPPORTED, "too many rows for one launch (%lld)", (long long)(tokens * Hsum));
     if (c->host_only) return host_only_launch(c);
     if (tokens == 0) return ULY_OK;
     a.cos_tab = cos_tab;
@@ -794,6 +824,9 @@ uly_status fused_qkv_proj_norm_rope_scatter(uly_ctx *c, const void *x, int dtype
     if (dtype != ULY_F16 && dtype != ULY_BF16) return fail(ULY_E_DTYPE, "the projection takes 16-bit floats");
     if (B < 0 || S_l < 0) return fail(ULY_E_INVAL, "negative B or S_l");
     if (Hq < 1 || Hkv < 1) return fail(ULY_E_INVAL, "q and k/v need at least one head each");
+    if (checked_prod({c->P, B, S_l}) < 0 || checked_prod({c->P, S_l}) < 0 || Hq > kMaxExtent ||
+        Hkv > kMaxExtent || hidden > kMaxExtent || table_rows > kMaxExtent)
+        return fail(ULY_E_UNSUPPORTED, "too large for one launch");
     if (Hq % c->P != 0 || Hkv % c->P != 0)
         return fail(ULY_E_INVAL, "heads (%lld, %lld) not divisible by world size %d", (long long)Hq,
                     (long long)Hkv, c->P);
@@ -814,8 +847,9 @@ uly_status fused_qkv_proj_norm_rope_scatter(uly_ctx *c, const void *x, int dtype
     const int64_t M = int64_t(c->P) * B * S_l, N = (Hq + 2 * Hkv) * D;
     const int64_t tiles = (M + kProjTileT - 1) / kProjTileT, NH = Hq + 2 * Hkv;
     const int64_t NHB = (NH + kProjHeads - 1) / kProjHeads;
-    if (M >= (int64_t(1) << 31) || tiles * NHB >= (int64_t(1) << 31) || hidden >= (int64_t(1) << 31) ||
-        M * hidden / 8 >= (int64_t(1) << 31) || N * hidden / 8 >= (int64_t(1) << 31))
+    const int64_t MK = checked_prod({M, hidden}), NK = checked_prod({N, hidden}), TB = checked_prod({tiles, NHB});
+    constexpr int64_t k2G = int64_t(1) << 31;
+    if (M >= k2G || hidden >= k2G || MK < 0 || NK < 0 || TB < 0 || TB >= k2G || MK / 8 >= k2G || NK / 8 >= k2G)
         return fail(ULY_E_UNSUPPORTED, "too large for one launch");
     const char *names[3] = {"q", "k", "v"};
     const int64_t heads[3] = {Hq, Hkv, Hkv};
@@ -932,8 +966,8 @@ uly_status uly_exchange_chunks(uly_ctx *c, const void *x, void *y, int64_t chunk
     if (st != ULY_OK) return st;
     if (chunk_bytes < 0 || chunk_bytes % 16 != 0)
         return fail(ULY_E_INVAL, "chunk of %lld bytes is not a non-negative multiple of 16", (long long)chunk_bytes);
-    const int64_t P = c->P, total_bytes = P * P * chunk_bytes;
-    if (total_bytes / 16 >= kMaxVecs) return fail(ULY_E_UNSUPPORTED, "too large for one launch");
+    const int64_t P = c->P, total_bytes = checked_prod({P, P, chunk_bytes});
+    if (total_bytes < 0 || total_bytes / 16 >= kMaxVecs) return fail(ULY_E_UNSUPPORTED, "too large for one launch");
     CopyBatch batch{};
     if (total_bytes > 0) {
         if (!x || !y || !aligned16(x) || !aligned16(y)) return fail(ULY_E_INVAL, "x, y null or not 16-byte aligned");
@@ -962,13 +996,14 @@ static uly_status rowmap_common(uly_ctx *c, const void *src, int dtype, int64_t 
     if (st != ULY_OK) return st;
     if (!valid_dtype(dtype)) return fail(ULY_E_DTYPE, "bad dtype %d", dtype);
     const int64_t es = elem_size(dtype);
-    if (row_elems < 1 || (row_elems * es) % 16 != 0)
+    if (row_elems < 1 || row_elems > kMaxExtent || (row_elems * es) % 16 != 0)
         return fail(ULY_E_INVAL, "row of %lld elements is not a positive multiple of 16 bytes",
                     (long long)row_elems);
-    if (src_rows < 0 || dst_rows < 0) return fail(ULY_E_INVAL, "negative extent");
+    if (src_rows < 0 || dst_rows < 0) return fail(ULY_E_INVAL, "negative or too large extent");
     const int64_t vpr = row_elems * es / 16;
-    const int64_t total = dst_rows * vpr;
-    if (total >= kMaxVecs || src_rows * vpr >= kMaxVecs) return fail(ULY_E_UNSUPPORTED, "too large for one launch");
+    const int64_t total = checked_prod({dst_rows, vpr}), src_total = checked_prod({src_rows, vpr});
+    if (total < 0 || src_total < 0 || total >= kMaxVecs || src_total >= kMaxVecs)
+        return fail(ULY_E_UNSUPPORTED, "too large for one launch");
     if (total > 0) {
         if (!dst || !aligned16(dst)) return fail(ULY_E_INVAL, "destination null or not 16-byte aligned");
         if (src_rows > 0 && (!src || !aligned16(src))) return fail(ULY_E_INVAL, "source null or not 16-byte aligned");
@@ -993,10 +1028,12 @@ static uly_status rowmap_launch(uly_ctx *c, const RowMapArgs &a, int rkind, int 
 
 uly_status uly_seq_pad_shard(uly_ctx *c, const void *full, int dtype, int64_t B, int64_t S, int64_t row_elems,
                              int64_t S_l, void *x, hipStream_t stream) {
-    if (c && (B < 0 || S < 0 || S_l < 0 || int64_t(c->P) * S_l < S))
+    if (c && (B < 0 || S < 0 || S_l < 0 || S_l > kMaxExtent || int64_t(c->P) * S_l < S))
         return fail(ULY_E_INVAL, "need B, S >= 0 and P*S_l >= S");
     RowMapArgs a;
-    uly_status st = rowmap_common(c, full, dtype, row_elems, x, B * S, int64_t(c ? c->P : 0) * B * S_l, a);
+    // an overflowing product comes back as -1, which rowmap_common rejects
+    uly_status st = rowmap_common(c, full, dtype, row_elems, x, checked_prod({B, S}),
+                                  checked_prod({c ? c->P : 0, B, S_l}), a);
     if (st != ULY_OK) return st;
     a.f0 = FastDiv::make(uint32_t(S_l));
     a.f1 = FastDiv::make(uint32_t(B));
@@ -1008,10 +1045,11 @@ uly_status uly_seq_pad_shard(uly_ctx *c, const void *full, int dtype, int64_t B,
 
 uly_status uly_seq_unshard_trim(uly_ctx *c, const void *x, int dtype, int64_t B, int64_t S, int64_t row_elems,
                                 int64_t S_l, void *full, hipStream_t stream) {
-    if (c && (B < 0 || S < 0 || S_l < 0 || int64_t(c->P) * S_l < S))
+    if (c && (B < 0 || S < 0 || S_l < 0 || S_l > kMaxExtent || int64_t(c->P) * S_l < S))
         return fail(ULY_E_INVAL, "need B, S >= 0 and P*S_l >= S");
     RowMapArgs a;
-    uly_status st = rowmap_common(c, x, dtype, row_elems, full, int64_t(c ? c->P : 0) * B * S_l, B * S, a);
+    uly_status st = rowmap_common(c, x, dtype, row_elems, full, checked_prod({c ? c->P : 0, B, S_l}),
+                                  checked_prod({B, S}), a);
     if (st != ULY_OK) return st;
     a.f0 = FastDiv::make(uint32_t(S));
     a.f2 = FastDiv::make(uint32_t(S_l));
@@ -1025,7 +1063,8 @@ uly_status uly_seq_unshard_trim(uly_ctx *c, const void *x, int dtype, int64_t B,
 
 static uly_status spatial_dims(uly_ctx *c, int64_t N, int64_t Hh, int64_t W, int64_t halo, int64_t &hmax) {
     if (!c) return fail(ULY_E_INVAL, "null context");
-    if (N < 0 || Hh < 1 || W < 1 || halo < 0) return fail(ULY_E_INVAL, "bad spatial extents");
+    if (N < 0 || Hh < 1 || W < 1 || halo < 0 || N > kMaxExtent || Hh > kMaxExtent || W > kMaxExtent)
+        return fail(ULY_E_INVAL, "bad spatial extents");
     if (Hh < c->P) return fail(ULY_E_INVAL, "height %lld smaller than world size %d", (long long)Hh, c->P);
     hmax = (Hh + c->P - 1) / c->P;
     if (halo > hmax) return fail(ULY_E_INVAL, "halo larger than a shard");
@@ -1048,7 +1087,9 @@ uly_status uly_spatial_split_halo(uly_ctx *c, const void *full, int dtype, int64
     if (st != ULY_OK) return st;
     RowMapArgs a;
     const int64_t R2 = hmax + 2 * halo;
-    if ((st = rowmap_common(c, full, dtype, W, shards, N * Hh, int64_t(c->P) * N * R2, a)) != ULY_OK) return st;
+    if ((st = rowmap_common(c, full, dtype, W, shards, checked_prod({N, Hh}), checked_prod({c->P, N, R2}), a)) !=
+        ULY_OK)
+        return st;
     a.f0 = FastDiv::make(uint32_t(R2));
     a.f1 = FastDiv::make(uint32_t(N));
     spatial_fill(a, c->P, N, Hh, hmax, halo);
@@ -1062,8 +1103,8 @@ uly_status uly_spatial_gather_stacked(uly_ctx *c, const void *shards, int dtype,
     if (st != ULY_OK) return st;
     RowMapArgs a;
     const int64_t R2 = hmax + 2 * halo;
-    if ((st = rowmap_common(c, shards, dtype, W, stacked, int64_t(c->P) * N * R2, int64_t(c->P) * N * hmax, a)) !=
-        ULY_OK)
+    if ((st = rowmap_common(c, shards, dtype, W, stacked, checked_prod({c->P, N, R2}), checked_prod({c->P, N, hmax}),
+                            a)) != ULY_OK)
         return st;
     a.f0 = FastDiv::make(uint32_t(hmax));
     a.f1 = FastDiv::make(uint32_t(N));
@@ -1077,7 +1118,9 @@ uly_status uly_spatial_trim_concat(uly_ctx *c, const void *stacked, int dtype, i
     uly_status st = spatial_dims(c, N, Hh, W, 0, hmax);
     if (st != ULY_OK) return st;
     RowMapArgs a;
-    if ((st = rowmap_common(c, stacked, dtype, W, full, int64_t(c->P) * N * hmax, N * Hh, a)) != ULY_OK) return st;
+    if ((st = rowmap_common(c, stacked, dtype, W, full, checked_prod({c->P, N, hmax}), checked_prod({N, Hh}), a)) !=
+        ULY_OK)
+        return st;
     a.f0 = FastDiv::make(uint32_t(Hh));
     a.f2 = FastDiv::make(uint32_t(Hh / c->P + 1));
     a.f3 = FastDiv::make(uint32_t(Hh / c->P));
@@ -1089,7 +1132,8 @@ uly_status uly_spatial_trim_concat(uly_ctx *c, const void *stacked, int dtype, i
 
 uly_status uly_rope_table_1d(float *cos_out, float *sin_out, int64_t rows, int64_t real_rows, int64_t D,
                              double theta) {
-    if (!cos_out || !sin_out || rows < 0 || real_rows < 0 || D < 2 || D % 2 || !(theta > 0))
+    if (!cos_out || !sin_out || rows < 0 || real_rows < 0 || D < 2 || D % 2 || !(theta > 0) ||
+        checked_prod({rows, D}) < 0)
         return fail(ULY_E_INVAL, "bad rope table arguments");
     const int64_t half = D / 2;
     std::vector<double> inv_freq(half);
@@ -1107,7 +1151,8 @@ uly_status uly_rope_table_1d(float *cos_out, float *sin_out, int64_t rows, int64
 uly_status uly_rope_table_3d(float *cos_out, float *sin_out, int64_t rows, int64_t real_rows, int64_t D,
                              int64_t grid_h, int64_t grid_w, int64_t n_t, int64_t n_h, int64_t n_w, double theta) {
     if (!cos_out || !sin_out || rows < 0 || real_rows < 0 || D < 2 || D % 2 || grid_h < 1 || grid_w < 1 ||
-        n_t < 0 || n_h < 0 || n_w < 0 || n_t + n_h + n_w > D / 2 || !(theta > 0))
+        n_t < 0 || n_h < 0 || n_w < 0 || n_t + n_h + n_w > D / 2 || !(theta > 0) || checked_prod({rows, D}) < 0 ||
+        checked_prod({grid_h, grid_w}) < 0)
         return fail(ULY_E_INVAL, "bad 3-D rope table arguments");
     const int64_t half = D / 2;
     const int64_t band_start[3] = {0, n_t, n_t + n_h};

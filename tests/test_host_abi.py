@@ -286,6 +286,45 @@ def test_launch_size_limits(lib, ctx4):
     assert b"too many rows" in lib.uly_last_error()
 
 
+def test_wrapping_sizes_refused(lib, ctx4):
+    """Extents whose products pass int64 are refused, never wrapped into a small launch."""
+    huge = 1 << 62
+    big_s = T(BASE, (1, huge, 8, 128), stride=(0, 1024, 128, 1), rank_stride=0)
+    assert scatter(lib, ctx4, q=big_s, tags=(None, None, None), outs=(BASE + 64 * MiB, None, None)) == _lib.E_UNSUPPORTED
+    assert b"too large" in lib.uly_last_error()
+    # B * S * H * D * 2 wraps to exactly 2^64 * k: 2^16 * 2^16 * 2^16 * 2^16 * 2
+    wrap = T(BASE, (1 << 16, 1 << 16, 1 << 16, 1 << 16))
+    assert scatter(lib, ctx4, q=wrap, tags=(None, None, None), outs=(BASE + 64 * MiB, None, None)) == _lib.E_UNSUPPORTED
+    # a stride whose span passes int64 once scaled by the element size
+    far = T(BASE, (2, 16, 8, 128), stride=(huge, 1024, 128, 1))
+    assert scatter(lib, ctx4, q=far, tags=(None, None, None), outs=(BASE + 64 * MiB, None, None)) == _lib.E_UNSUPPORTED
+    o = T(BASE, (1 << 20, 1 << 22, 1 << 20, 128))
+    assert lib.ulysses_gather_out(ctx4.h, ctypes.byref(o), None, BASE + 64 * MiB, None) == _lib.E_UNSUPPORTED
+    qf = T(BASE, (1 << 30, 1 << 30, 32, 32))
+    assert _fused(lib, ctx4, qf, qf, outs=(BASE + 64 * MiB, BASE + 128 * MiB)) == _lib.E_UNSUPPORTED
+    assert b"too large" in lib.uly_last_error()
+    qs, ks = T(BASE, (1, 16, 8, 128)), T(BASE + 8 * MiB, (1, 16, 8, 128))
+    assert _fused(lib, ctx4, qs, ks, rows=huge) == _lib.E_UNSUPPORTED and b"table" in lib.uly_last_error()
+    # projection: P * B * S_l and M * hidden would wrap
+    assert _proj(lib, ctx4, B=1 << 40, S_l=1 << 40, rows=huge) == _lib.E_UNSUPPORTED
+    assert _proj(lib, ctx4, B=1, S_l=1 << 20, hidden=1 << 50, rows=1 << 22) == _lib.E_UNSUPPORTED
+    assert _proj(lib, ctx4, Hq=1 << 60, Hkv=4) == _lib.E_UNSUPPORTED
+    # row maps, the chunk exchange and the host tables
+    assert lib.uly_seq_pad_shard(ctx4.h, BASE, _lib.BF16, 1 << 40, 1 << 40, 64, 1 << 38, BASE + 64 * MiB,
+                                 None) == _lib.E_INVAL
+    assert lib.uly_seq_unshard_trim(ctx4.h, BASE, _lib.BF16, huge, 4, 64, 1, BASE + 64 * MiB, None) == _lib.E_INVAL
+    assert lib.uly_spatial_split_halo(ctx4.h, BASE, _lib.BF16, 1 << 40, 1 << 40, 64, 0, BASE + 64 * MiB,
+                                      None) == _lib.E_INVAL
+    assert lib.uly_exchange_chunks(ctx4.h, BASE, BASE + 64 * MiB, 1 << 60, None) == _lib.E_UNSUPPORTED
+    cos = np.zeros(4, np.float32)
+    fp = cos.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    assert lib.uly_rope_table_1d(fp, fp, huge, 0, 128, 10000.0) == _lib.E_INVAL
+    assert lib.uly_rope_table_3d(fp, fp, 1, 0, 128, huge, huge, 16, 24, 24, 10000.0) == _lib.E_INVAL
+    # the world size is bounded
+    h = ctypes.c_void_p()
+    assert lib.uly_create(ctypes.byref(h), -1, 1 << 30, 12) == _lib.E_INVAL
+
+
 def test_fail_stop_after_launch_failure(lib):
     c = Ctx(lib, 2)
     try:
