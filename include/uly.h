@@ -56,6 +56,11 @@
  *   ULY_E_HIP and poisons the context: every later call returns
  *   ULY_E_BROKEN and only uly_destroy is allowed (fail-stop).
  *   uly_last_error() returns a thread-local message for the last failure.
+ *   Extents, strides, table lengths and the sizes formed from them are
+ *   bounded by 2^48 (elements or bytes) and checked without wrapping;
+ *   larger ones are refused (ULY_E_UNSUPPORTED, or ULY_E_INVAL for the row
+ *   maps and host tables), as are launches past the 32-bit index limits
+ *   that each entry point states.
  *
  * Streams.  The context owns one extra HIP stream ("comm stream", default
  *   priority) on which the plain Q/K/V scatter runs, so that it overlaps
@@ -123,8 +128,9 @@ typedef struct {
 
 /* ---- context ---------------------------------------------------------- */
 
-/* Create a context for `world_size` emulated ranks on HIP device `device`
- * with room for `max_targets` cached targets (1..12, [P27 "Changes Made"]).
+/* Create a context for `world_size` emulated ranks (1..4096) on HIP device
+ * `device` with room for `max_targets` cached targets (1..12, [P27 "Changes
+ * Made"]).
  * device = -1 creates a host-only context: argument checks and the target
  * cache work, every call that would enqueue GPU work returns
  * ULY_E_UNSUPPORTED after its checks pass. */
