@@ -944,3 +944,21 @@ def test_projection_gqa_full(dev, orc):
         ctx.wait()
         torch.cuda.synchronize()
         _check_proj_sampled(orc, x, w, wq, wk, ys, Hq, Hkv, "bf16", ocos, osin, [(0, 1), (8191, 1)])
+
+
+def test_projection_wan_full(dev, orc):
+    """Wan-style long sequence (P=4, S=75600 padded to 75776, H=40, hidden 5120, bf16, 3-D
+    RoPE with pad rows) at full size, sampled; its 776 MB activations take the three-stage
+    token-row ring."""
+    from sequence_attention_ulysses_amd import rope_table_3d
+    P, B, S_l, H, hidden = 4, 1, 18944, 40, 5120
+    S_real, Hh, Ww = 75600, 60, 60
+    x, w, wq, wk = _proj_inputs(P, B, S_l, hidden, H, H, "bf16", 90, dev)
+    cos, sin = rope_table_3d(P * S_l, 128, Hh, Ww, real_rows=S_real)
+    ocos, osin = orc.rope_table_3d(P * S_l, 128, Hh, Ww, real_rows=S_real)
+    with UlyssesContext(P, device=0) as ctx:
+        ys = ctx.fused_qkv_proj_norm_rope_scatter(x, w, H, H, wq, wk, cos.to(dev), sin.to(dev))
+        ctx.wait()
+        torch.cuda.synchronize()
+        # on rank 3 the window at 18766 holds positions 75598..75601: two real rows, two pad rows
+        _check_proj_sampled(orc, x, w, wq, wk, ys, H, H, "bf16", ocos, osin, [(0, 1), (9000, 1), (18766, 4)])
