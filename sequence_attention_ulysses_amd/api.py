@@ -77,6 +77,17 @@ def rope_table_3d(rows: int, D: int, grid_h: int, grid_w: int, pairs=(22, 21, 21
     return cos, sin
 
 
+def _check_tables(cos, sin, D: int | None) -> None:
+    """cos and sin: contiguous fp32 [rows, D/2] of one shape (the library reads `rows` rows of each)."""
+    for t in (cos, sin):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError("cos/sin tables must be contiguous fp32 [rows, D/2]")
+    if cos.shape != sin.shape:
+        raise ValueError("cos and sin tables differ in shape")
+    if D is not None and cos.shape[1] * 2 != D:
+        raise ValueError("cos/sin tables must have D/2 columns")
+
+
 def height_split(Hh: int, P: int):
     """Heights of the P height shards (the first Hh % P ranks take one more row) and hmax."""
     base, extra = divmod(Hh, P)
@@ -215,6 +226,7 @@ class UlyssesContext:
         """
         P = self.world_size
         mem = (q, k, v)
+        _check_tables(cos, sin, None)
         self._on_device(q, k, v, w_q, w_k, cos, sin)
         descs, dests, ptrs = [], [], []
         for i, x in enumerate(mem):
@@ -229,11 +241,6 @@ class UlyssesContext:
             d, explicit = self._dest(tags[i], _lib.MODE_SCATTER, x, shape, o_i)
             descs.append(describe(x)); dests.append(d)
             ptrs.append(d.data_ptr() if explicit else None)
-        for t in (cos, sin):
-            if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2:
-                raise ValueError("cos/sin tables must be contiguous fp32 [rows, D/2]")
-        if cos.shape != sin.shape:
-            raise ValueError("cos and sin tables differ in shape")
         args = [ctypes.byref(dd) if dd is not None else None for dd in descs]
         wq = w_q.data_ptr() if (w_q is not None and q is not None) else None
         wk = w_k.data_ptr() if (w_k is not None and k is not None) else None
@@ -260,6 +267,7 @@ class UlyssesContext:
         Returns the destination tensors (q, k, v), [P, B, P*S_l, H/P, D] each.
         """
         P = self.world_size
+        _check_tables(cos, sin, w_q.numel())
         self._on_device(x, w_qkv, w_q, w_k, cos, sin)
         if x.dim() != 4 or not x.is_contiguous() or not w_qkv.is_contiguous() or w_qkv.dim() != 2:
             raise ValueError("x must be a contiguous [P, B, S_l, hidden] tensor and w_qkv a contiguous matrix")
@@ -271,9 +279,6 @@ class UlyssesContext:
         for w in (w_q, w_k):
             if w.dtype != x.dtype or not w.is_contiguous() or w.numel() != D:
                 raise ValueError("norm weights must be contiguous [D] tensors in the activation dtype")
-        for t in (cos, sin):
-            if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2 or t.shape[1] * 2 != D:
-                raise ValueError("cos/sin tables must be contiguous fp32 [rows, D/2]")
         B, S_l = x.shape[1], x.shape[2]
         dests, ptrs = [], []
         for i, H in enumerate((Hq, Hkv, Hkv)):
@@ -295,6 +300,7 @@ class UlyssesContext:
         """Q/K norm + RoPE scatter with V into one packed target [P, B, P*S_l, H/P, 3*D]:
         each head row holds q, k and v side by side."""
         P = self.world_size
+        _check_tables(cos, sin, q.shape[-1])
         self._on_device(q, k, v, w_q, w_k, cos, sin, out)
         for x in (q, k, v):
             if x.dim() != 5:
@@ -310,9 +316,6 @@ class UlyssesContext:
         for w in (w_q, w_k):
             if w.dtype != q.dtype or not w.is_contiguous() or w.numel() != q.shape[-1]:
                 raise ValueError("norm weights must be contiguous [D] tensors in the operand dtype")
-        for t in (cos, sin):
-            if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2 or t.shape[1] * 2 != q.shape[-1]:
-                raise ValueError("cos/sin tables must be contiguous fp32 [rows, D/2]")
         check(self._lib.fused_qkv_norm_rope_scatter_packed(
             self._h(), ctypes.byref(describe(q)), ctypes.byref(describe(k)), ctypes.byref(describe(v)),
             w_q.data_ptr(), w_k.data_ptr(), float(eps), cos.data_ptr(), sin.data_ptr(), cos.shape[0],

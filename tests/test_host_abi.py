@@ -422,6 +422,32 @@ def test_python_binding_host_only():
     c2.close()
 
 
+def test_binding_table_checks():
+    """The three norm + RoPE bindings pass cos's row count for both tables, so they
+    refuse tables of different shapes (or the wrong width) before anything else."""
+    import torch
+
+    from sequence_attention_ulysses_amd import UlyssesContext
+    c = UlyssesContext(2, device=None)
+    try:
+        q = torch.zeros((2, 1, 8, 2, 128), dtype=torch.bfloat16)
+        w = torch.ones(128, dtype=torch.bfloat16)
+        x = torch.zeros((2, 1, 8, 256), dtype=torch.bfloat16)
+        wqkv = torch.zeros((6 * 128, 256), dtype=torch.bfloat16)
+        good = torch.zeros((16, 64), dtype=torch.float32)
+        for cos, sin, msg in ((good, torch.zeros((15, 64)), "differ"), (torch.zeros((16, 32)),) * 2 + ("D/2",),
+                              (good, good.double(), "fp32")):
+            with pytest.raises(ValueError, match=msg):
+                c.fused_qkv_norm_rope_scatter_packed(q, q, q, w, w, cos, sin)
+            with pytest.raises(ValueError, match=msg):
+                c.fused_qkv_proj_norm_rope_scatter(x, wqkv, 2, 2, w, w, cos, sin)
+            if msg != "D/2":       # this binding checks the width against each operand later
+                with pytest.raises(ValueError, match=msg):
+                    c.fused_qk_norm_rope_scatter(q, q, w, w, cos, sin)
+    finally:
+        c.close()
+
+
 def test_profile_arguments(lib, ctx4):
     assert lib.uly_profile_enable(ctx4.h, 0x3, 0) == _lib.E_INVAL
     assert lib.uly_profile_enable(ctx4.h, 0x3, 4) == _lib.OK
