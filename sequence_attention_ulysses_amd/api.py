@@ -160,6 +160,8 @@ class UlyssesContext:
         Returns a [P, *shape] view of the registered storage.  When the cache
         is full the returned tensor is a one-shot buffer (not cached).
         """
+        if not tag:
+            raise ValueError("a cached target needs a tag (or pass an explicit destination)")
         shape = tuple(int(s) for s in shape)
         code = _dtype_code(dtype)
         key = (tag, mode, code, shape)           # the library's key: 1-byte types share one code

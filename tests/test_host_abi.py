@@ -448,6 +448,20 @@ def test_binding_table_checks():
         c.close()
 
 
+def test_binding_needs_tag_or_destination():
+    """Without an explicit destination a member must name a cached target."""
+    import torch
+
+    from sequence_attention_ulysses_amd import UlyssesContext
+    c = UlyssesContext(2, device=None)
+    try:
+        for tag in (None, ""):
+            with pytest.raises(ValueError, match="needs a tag"):
+                c.target(tag, _lib.MODE_SCATTER, torch.bfloat16, (1, 8, 2, 64))
+    finally:
+        c.close()
+
+
 def test_profile_arguments(lib, ctx4):
     assert lib.uly_profile_enable(ctx4.h, 0x3, 0) == _lib.E_INVAL
     assert lib.uly_profile_enable(ctx4.h, 0x3, 4) == _lib.OK
