@@ -8,15 +8,31 @@ resident in HBM:
   2. the grouped wait,
   3. the attention output gathered back from head-sharded to
      sequence-sharded.
-The two-stream form of step 1 (V on the library's comm stream overlapping
-the fused Q/K kernel on the caller's stream) is timed alongside and reported
-under "two_stream".
 
 Workload: the video-DiT block with P=4 emulated ranks, B=1, S_local=4096
 (S=16384), H=24, D=128, bf16, V strided from the fused QKV projection.  The
 metric is algorithmic bytes per step (each input element read once and each
-output element written once: 805,306,368 B) over wall time, in GB/s, and as
-a fraction of the 8 TB/s HBM peak.
+output element written once: 805,306,368 B) over the step's time, in GB/s,
+and as a fraction of the 8 TB/s HBM peak.
+
+Timing (flashinfer PR #6332 times with a cold L2, "Speedup", and gates its
+records, "Export-protocol validation"):
+  * the timed steps rotate over three independent sets of inputs and
+    destinations (--sets), so nothing a step reads is still cached from the
+    step before, and they run back to back with HIP events between them, so
+    every byte a step writes is charged to the steps (a write-back still in
+    flight when a step's last kernel ends delays the next step);
+  * the headline is the median of exactly --steps such steps (p10 and p90
+    beside it);
+  * an A/A repeat of the same measurement that drifts by more than 2 %
+    marks the record invalid, with the reason;
+  * the dominant kernel is timed on at least 10 launches by the library's
+    own events on the stream it runs on (the roofline figure);
+  * reported beside it: the host's enqueue time per step, a warm wall-clock
+    loop on one set, the step after a 1 GiB cache-evicting read with events
+    around the step alone (that form lets dirty lines left in the caches be
+    written back outside the events), the two-stream form of step 1 and
+    copy controls.
 
 Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
 """
@@ -34,7 +50,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Ulysses QKV scatter+gather GB/s and % HBM peak, P=4 bf16, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
-PROFILE_EVERY = 16
+AA_MAX_DRIFT = 0.02          # an A/A repeat further off than this voids the record
+MIN_TIMED_LAUNCHES = 10      # launches of the dominant kernel timed whatever --steps is
 KERNEL_SOURCES = [os.path.join(ROOT, "sequence_attention_ulysses_amd", "csrc", f)
                   for f in ("uly_kernels.hip", "uly_internal.h", "fastdiv.h")]
 
@@ -129,117 +146,156 @@ def cpu_baseline(args, inputs, min_seconds: float = 10.0):
 
 
 # ---------------------------------------------------------------------------
-# Workloads.  Each setup returns the context, the step (and its two-stream
-# form where there is one), the algorithmic bytes of a step (each input
-# element read once, each output element written once, real tokens only),
-# the dominant kernel (kind, bytes per launch, name) and the JSON config.
+# Workloads.  Each setup builds `sets` independent sets of inputs and
+# explicit destinations (different seeds, distinct buffers) and returns one
+# step closure per set, so that consecutive timed steps touch disjoint memory
+# and nothing a step reads is still in a cache from the step before (two
+# other sets, >= 1.5 GiB, pass between two uses of a set: far more than the
+# 256 MB Infinity Cache).  Also returned: the algorithmic bytes of a step
+# (each input element read once, each output element written once, real
+# tokens only), the dominant kernel (kind, bytes per launch, name) and the
+# JSON config.
 # ---------------------------------------------------------------------------
-def setup_video_dit(torch, dev, synth, rope_table_1d, UlyssesContext, dtype="bf16"):
+def _empty(torch, dev, shape, dtype):
+    return torch.empty(tuple(shape), dtype=dtype, device=dev)
+
+
+def setup_video_dit(torch, dev, synth, rope_table_1d, UlyssesContext, sets=3, dtype="bf16"):
     w = synth.VIDEO_DIT
     P, B, S_l, H, D = w.P, w.B, w.S_l, w.Hq, w.D
     n_tensor = P * B * S_l * H * D * 2
-    qkv = synth.normal((P, B, S_l, 3, H, D), dtype, 0)
-    w_q, w_k = synth.norm_weight(D, dtype, 1), synth.norm_weight(D, dtype, 2)
-    o = synth.normal((P, B, P * S_l, H // P, D), dtype, 3)
+    tdt = synth.DTYPES[dtype]
     cos, sin = rope_table_1d(P * S_l, D, theta=w.theta)
-    g_qkv, g_wq, g_wk, g_o = qkv.to(dev), w_q.to(dev), w_k.to(dev), o.to(dev)
     g_cos, g_sin = cos.to(dev), sin.to(dev)
-    q_in, k_in, v_in = g_qkv[:, :, :, 0], g_qkv[:, :, :, 1], g_qkv[:, :, :, 2]
     ctx = UlyssesContext(P, device=0)
+    steps, two_stream, cpu_inputs = [], [], None
+    for k in range(sets):
+        if k == 0:       # set 0 is drawn on the host too: the CPU oracle times the same inputs
+            qkv = synth.normal((P, B, S_l, 3, H, D), dtype, 0)
+            w_q, w_k = synth.norm_weight(D, dtype, 1), synth.norm_weight(D, dtype, 2)
+            o = synth.normal((P, B, P * S_l, H // P, D), dtype, 3)
+            cpu_inputs = (qkv, w_q, w_k, o)
+            g_qkv, g_wq, g_wk, g_o = qkv.to(dev), w_q.to(dev), w_k.to(dev), o.to(dev)
+        else:
+            g_qkv = synth.normal((P, B, S_l, 3, H, D), dtype, 10 * k, dev)
+            g_wq, g_wk = synth.norm_weight(D, dtype, 10 * k + 1, dev), synth.norm_weight(D, dtype, 10 * k + 2, dev)
+            g_o = synth.normal((P, B, P * S_l, H // P, D), dtype, 10 * k + 3, dev)
+        yq, yk, yv = (_empty(torch, dev, (P, B, P * S_l, H // P, D), tdt) for _ in range(3))
+        z = _empty(torch, dev, (P, B, S_l, H, D), tdt)
 
-    def step():
-        ctx.fused_qk_norm_rope_scatter(q_in, k_in, g_wq, g_wk, g_cos, g_sin, eps=w.eps, v=v_in)
-        ctx.wait()
-        ctx.gather_out(g_o)
+        def step(q=g_qkv[:, :, :, 0], k_=g_qkv[:, :, :, 1], v=g_qkv[:, :, :, 2], wq=g_wq, wk=g_wk, o=g_o,
+                 outs=(yq, yk, yv), z=z):
+            ctx.fused_qk_norm_rope_scatter(q, k_, wq, wk, g_cos, g_sin, eps=w.eps, v=v, out=outs)
+            ctx.wait()
+            ctx.gather_out(o, out=z)
 
-    def step_two_stream():
-        ctx.scatter_qkv(v=v_in, tags=(None, None, "v2"))
-        ctx.fused_qk_norm_rope_scatter(q_in, k_in, g_wq, g_wk, g_cos, g_sin, eps=w.eps)
-        ctx.wait()
-        ctx.gather_out(g_o)
+        def step_two_stream(q=g_qkv[:, :, :, 0], k_=g_qkv[:, :, :, 1], v=g_qkv[:, :, :, 2], wq=g_wq, wk=g_wk,
+                            o=g_o, outs=(yq, yk, yv), z=z):
+            ctx.scatter_qkv(v=v, out=(None, None, outs[2]))
+            ctx.fused_qk_norm_rope_scatter(q, k_, wq, wk, g_cos, g_sin, eps=w.eps, out=(outs[0], outs[1], None))
+            ctx.wait()
+            ctx.gather_out(o, out=z)
 
-    return {"workload": w, "ctx": ctx, "step": step, "step_two_stream": step_two_stream,
+        steps.append(step)
+        two_stream.append(step_two_stream)
+    return {"workload": w, "ctx": ctx, "steps": steps, "two_stream": two_stream,
             "bytes_per_step": 3 * 2 * n_tensor + 2 * n_tensor,
             "dominant": ("norm_rope", 6 * n_tensor,
                          "norm_rope_kernel<16,bf16> (Q/K RMSNorm+RoPE scatter with V in the same grid)"),
-            "cpu_inputs": (qkv, w_q, w_k, o), "dtype": dtype,
+            "cpu_inputs": cpu_inputs, "dtype": dtype,
             "data": "synthetic N(0,1) activations, N(1,0.1) norm weights, 1-D RoPE theta 1e4 (seeded)",
             "config": {"workload": w.name, "P": P, "B": B, "S_local": S_l, "S": P * S_l, "H": H, "D": D,
                        "v_source": "strided from fused QKV [B,S_local,3,H,D]", "parallelism": "ulysses-p4-emulated",
                        "bytes_per_step": 3 * 2 * n_tensor + 2 * n_tensor}}
 
 
-def setup_wan_long(torch, dev, synth, rope_table_1d, UlyssesContext):
+def setup_wan_long(torch, dev, synth, rope_table_1d, UlyssesContext, sets=3):
     from sequence_attention_ulysses_amd import rope_table_3d
     w = synth.WAN_LONG
     P, B, S_l, H, D, S = w.P, w.B, w.S_l, w.Hq, w.D, w.S_real
     _, Hh, Ww = w.grid
     ctx = UlyssesContext(P, device=0)
-    # global sequences, padded and sharded once (the pad/trim kernels are not in the step)
-    shards = [ctx.seq_pad_shard(synth.normal((B, S, H, D), "bf16", 30 + i, dev), S_l) for i in range(3)]
-    w_q, w_k = synth.norm_weight(D, "bf16", 31, dev), synth.norm_weight(D, "bf16", 32, dev)
     cos, sin = (t.to(dev) for t in rope_table_3d(P * S_l, D, Hh, Ww, real_rows=S, theta=w.theta))
-    o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 33, dev)
     real = B * S * H * D * 2
+    steps = []
+    for k in range(sets):
+        # global sequences, padded and sharded once (the pad/trim kernels are not in the step)
+        shards = [ctx.seq_pad_shard(synth.normal((B, S, H, D), "bf16", 30 + 10 * k + i, dev), S_l) for i in range(3)]
+        w_q, w_k = synth.norm_weight(D, "bf16", 34 + 10 * k, dev), synth.norm_weight(D, "bf16", 35 + 10 * k, dev)
+        o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 36 + 10 * k, dev)
+        outs = tuple(_empty(torch, dev, (P, B, P * S_l, H // P, D), torch.bfloat16) for _ in range(3))
+        z = _empty(torch, dev, (P, B, S_l, H, D), torch.bfloat16)
 
-    def step():
-        ctx.fused_qk_norm_rope_scatter(shards[0], shards[1], w_q, w_k, cos, sin, eps=w.eps, v=shards[2])
-        ctx.wait()
-        ctx.gather_out(o)
+        def step(sh=shards, wq=w_q, wk=w_k, o=o, outs=outs, z=z):
+            ctx.fused_qk_norm_rope_scatter(sh[0], sh[1], wq, wk, cos, sin, eps=w.eps, v=sh[2], out=outs)
+            ctx.wait()
+            ctx.gather_out(o, out=z)
 
-    return {"workload": w, "ctx": ctx, "step": step, "bytes_per_step": 3 * 2 * real + 2 * real,
+        steps.append(step)
+    return {"workload": w, "ctx": ctx, "steps": steps, "bytes_per_step": 3 * 2 * real + 2 * real,
             "dominant": ("norm_rope", 6 * real, "norm_rope_kernel<16,bf16> (3-D RoPE, padded sequence)"),
             "dtype": "bf16", "data": "synthetic N(0,1) activations, N(1,0.1) norm weights, 3-D RoPE 44/42/42",
             "config": {"workload": w.name, "P": P, "B": B, "S": S, "S_padded": P * S_l, "H": H, "D": D,
                        "bytes_per_step": 3 * 2 * real + 2 * real, "bytes_count": "real tokens only"}}
 
 
-def setup_gqa(torch, dev, synth, rope_table_1d, UlyssesContext):
+def setup_gqa(torch, dev, synth, rope_table_1d, UlyssesContext, sets=3):
     w = synth.GQA
     P, B, S_l, Hq, Hkv, D = w.P, w.B, w.S_l, w.Hq, w.Hkv, w.D
-    q = synth.normal((P, B, S_l, Hq, D), "bf16", 40, dev)
-    k = synth.normal((P, B, S_l, Hkv, D), "bf16", 41, dev)
-    v = synth.normal((P, B, S_l, Hkv, D), "bf16", 42, dev)
-    o = synth.normal((P, B, P * S_l, Hq // P, D), "bf16", 43, dev)
     ctx = UlyssesContext(P, device=0)
     nq, nkv = P * B * S_l * Hq * D * 2, P * B * S_l * Hkv * D * 2
+    steps = []
+    for k in range(sets):
+        q = synth.normal((P, B, S_l, Hq, D), "bf16", 40 + 10 * k, dev)
+        k_ = synth.normal((P, B, S_l, Hkv, D), "bf16", 41 + 10 * k, dev)
+        v = synth.normal((P, B, S_l, Hkv, D), "bf16", 42 + 10 * k, dev)
+        o = synth.normal((P, B, P * S_l, Hq // P, D), "bf16", 43 + 10 * k, dev)
+        outs = (_empty(torch, dev, (P, B, P * S_l, Hq // P, D), torch.bfloat16),
+                _empty(torch, dev, (P, B, P * S_l, Hkv // P, D), torch.bfloat16),
+                _empty(torch, dev, (P, B, P * S_l, Hkv // P, D), torch.bfloat16))
+        z = _empty(torch, dev, (P, B, S_l, Hq, D), torch.bfloat16)
 
-    def step():
-        ctx.scatter_qkv(q, k, v)
-        ctx.wait()
-        ctx.gather_out(o)
+        def step(q=q, k_=k_, v=v, o=o, outs=outs, z=z):
+            ctx.scatter_qkv(q, k_, v, out=outs)
+            ctx.wait()
+            ctx.gather_out(o, out=z)
 
-    return {"workload": w, "ctx": ctx, "step": step, "bytes_per_step": 2 * (nq + 2 * nkv) + 2 * nq,
+        steps.append(step)
+    return {"workload": w, "ctx": ctx, "steps": steps, "bytes_per_step": 2 * (nq + 2 * nkv) + 2 * nq,
             "dominant": ("scatter", 2 * (nq + 2 * nkv), "relayout_kernel (grouped Q/K/V scatter, one launch)"),
             "dtype": "bf16", "data": "synthetic N(0,1) activations",
             "config": {"workload": w.name, "P": P, "B": B, "S_local": S_l, "Hq": Hq, "Hkv": Hkv, "D": D,
                        "bytes_per_step": 2 * (nq + 2 * nkv) + 2 * nq}}
 
 
-def setup_tiny(torch, dev, synth, rope_table_1d, UlyssesContext):
+def setup_tiny(torch, dev, synth, rope_table_1d, UlyssesContext, sets=3):
     w = synth.TINY
     P, B, S_l, H, D = w.P, w.B, w.S_l, w.Hq, w.D
-    q, k, v = (synth.normal((P, B, S_l, H, D), "f16", 50 + i, dev) for i in range(3))
-    o = synth.normal((P, B, P * S_l, H // P, D), "f16", 53, dev)
     ctx = UlyssesContext(P, device=0)
     n = P * B * S_l * H * D * 2
+    steps = []
+    for k in range(sets):
+        q, k_, v = (synth.normal((P, B, S_l, H, D), "f16", 50 + 10 * k + i, dev) for i in range(3))
+        o = synth.normal((P, B, P * S_l, H // P, D), "f16", 53 + 10 * k, dev)
+        outs = tuple(_empty(torch, dev, (P, B, P * S_l, H // P, D), torch.float16) for _ in range(3))
+        z = _empty(torch, dev, (P, B, S_l, H, D), torch.float16)
 
-    def step():
-        ctx.scatter_qkv(q, k, v)
-        ctx.wait()
-        ctx.gather_out(o)
+        def step(q=q, k_=k_, v=v, o=o, outs=outs, z=z):
+            ctx.scatter_qkv(q, k_, v, out=outs)
+            ctx.wait()
+            ctx.gather_out(o, out=z)
 
-    return {"workload": w, "ctx": ctx, "step": step, "bytes_per_step": 3 * 2 * n + 2 * n,
+        steps.append(step)
+    return {"workload": w, "ctx": ctx, "steps": steps, "bytes_per_step": 3 * 2 * n + 2 * n,
             "dominant": ("scatter", 6 * n, "relayout_kernel (grouped Q/K/V scatter, one launch)"),
             "dtype": "f16", "data": "synthetic N(0,1) activations",
             "config": {"workload": w.name, "P": P, "B": B, "S_local": S_l, "H": H, "D": D,
                        "bytes_per_step": 3 * 2 * n + 2 * n, "note": "launch-bound"}}
 
 
-def setup_spatial(torch, dev, synth, rope_table_1d, UlyssesContext):
+def setup_spatial(torch, dev, synth, rope_table_1d, UlyssesContext, sets=3):
     from sequence_attention_ulysses_amd import height_split
     w = synth.SPATIAL
-    full = synth.normal(w.shape, w.dtype, 60, dev)
     ctx = UlyssesContext(w.P, device=0)
     lead, (Hh, W) = w.shape[:-2], w.shape[-2:]
     N = 1
@@ -253,16 +309,20 @@ def setup_spatial(torch, dev, synth, rope_table_1d, UlyssesContext):
     split = N * row * (Hh + halo_rows) + N * row * w.P * (hmax + 2 * w.halo)
     gather = N * row * Hh + N * row * w.P * hmax
     trim = N * row * Hh * 2
+    steps = []
+    for k in range(sets):
+        full = synth.normal(w.shape, w.dtype, 60 + k, dev)
+        bufs = [_empty(torch, dev, (w.P,) + lead + (hmax + 2 * w.halo, W), full.dtype),
+                _empty(torch, dev, (w.P,) + lead + (hmax, W), full.dtype),
+                _empty(torch, dev, w.shape, full.dtype)]
 
-    def step():
-        sh = ctx.spatial_split_halo(full, halo=w.halo, out=bufs[0])
-        st = ctx.spatial_gather_stacked(sh, Hh, halo=w.halo, out=bufs[1])
-        ctx.spatial_trim_concat(st, Hh, out=bufs[2])
+        def step(full=full, bufs=bufs):
+            sh = ctx.spatial_split_halo(full, halo=w.halo, out=bufs[0])
+            st = ctx.spatial_gather_stacked(sh, Hh, halo=w.halo, out=bufs[1])
+            ctx.spatial_trim_concat(st, Hh, out=bufs[2])
 
-    bufs = [torch.empty((w.P,) + lead + (hmax + 2 * w.halo, W), dtype=full.dtype, device=dev),
-            torch.empty((w.P,) + lead + (hmax, W), dtype=full.dtype, device=dev),
-            torch.empty(w.shape, dtype=full.dtype, device=dev)]
-    return {"workload": w, "ctx": ctx, "step": step, "bytes_per_step": split + gather + trim,
+        steps.append(step)
+    return {"workload": w, "ctx": ctx, "steps": steps, "bytes_per_step": split + gather + trim,
             "dominant": ("spatial", (split + gather + trim) // 3, "rowmap_kernel (average of the three launches)"),
             "dtype": "bf16", "data": "synthetic N(0,1) latent",
             "config": {"workload": w.name, "P": w.P, "shape": list(w.shape), "heights": h, "halo": w.halo,
@@ -272,7 +332,7 @@ def setup_spatial(torch, dev, synth, rope_table_1d, UlyssesContext):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def _setup_proj(torch, dev, synth, rope_table_1d, UlyssesContext, w, seed, name):
+def _setup_proj(torch, dev, synth, rope_table_1d, UlyssesContext, w, seed, name, sets=3):
     """The attention front end with the QKV projection fused in: one launch
     projects x, normalises and rotates q/k and stores every head band into
     its head-sharded target (flashinfer PR #6332's fused call), then the wait
@@ -282,39 +342,47 @@ def _setup_proj(torch, dev, synth, rope_table_1d, UlyssesContext, w, seed, name)
     P, B, S_l, Hq, Hkv, D = w.P, w.B, w.S_l, w.Hq, w.Hkv, w.D
     hidden, N = Hq * D, (Hq + 2 * Hkv) * D
     M = P * B * S_l
-    x = synth.normal((P, B, S_l, hidden), "bf16", seed, dev)
     w_qkv = synth.normal((N, hidden), "bf16", seed + 1, dev, std=hidden ** -0.5)
     w_q, w_k = synth.norm_weight(D, "bf16", seed + 2, dev), synth.norm_weight(D, "bf16", seed + 3, dev)
     cos, sin = (t.to(dev) for t in rope_table_1d(P * S_l, D, theta=w.theta))
-    o = synth.normal((P, B, P * S_l, Hq // P, D), "bf16", seed + 4, dev)
     ctx = UlyssesContext(P, device=0)
     flops = 2 * M * N * hidden
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    y4 = y.view(P, B, S_l, N)
-    yq = y4[..., :Hq * D].unflatten(-1, (Hq, D))
-    yk = y4[..., Hq * D:(Hq + Hkv) * D].unflatten(-1, (Hkv, D))
-    yv = y4[..., (Hq + Hkv) * D:].unflatten(-1, (Hkv, D))
-    x2 = x.view(M, hidden)
+    bf = torch.bfloat16
+    steps, per_op, x0 = [], [], None
+    for k in range(sets):
+        x = synth.normal((P, B, S_l, hidden), "bf16", seed + 10 * k, dev)
+        x0 = x if k == 0 else x0
+        o = synth.normal((P, B, P * S_l, Hq // P, D), "bf16", seed + 10 * k + 4, dev)
+        outs = (_empty(torch, dev, (P, B, P * S_l, Hq // P, D), bf),
+                _empty(torch, dev, (P, B, P * S_l, Hkv // P, D), bf),
+                _empty(torch, dev, (P, B, P * S_l, Hkv // P, D), bf))
+        z = _empty(torch, dev, (P, B, S_l, Hq, D), bf)
+        y = _empty(torch, dev, (M, N), bf)
+        y4 = y.view(P, B, S_l, N)
+        yq = y4[..., :Hq * D].unflatten(-1, (Hq, D))
+        yk = y4[..., Hq * D:(Hq + Hkv) * D].unflatten(-1, (Hkv, D))
+        yv = y4[..., (Hq + Hkv) * D:].unflatten(-1, (Hkv, D))
 
-    def step():
-        ctx.fused_qkv_proj_norm_rope_scatter(x, w_qkv, Hq, Hkv, w_q, w_k, cos, sin, eps=w.eps)
-        ctx.wait()
-        ctx.gather_out(o)
+        def step(x=x, o=o, outs=outs, z=z):
+            ctx.fused_qkv_proj_norm_rope_scatter(x, w_qkv, Hq, Hkv, w_q, w_k, cos, sin, eps=w.eps, out=outs)
+            ctx.wait()
+            ctx.gather_out(o, out=z)
 
-    def step_per_operator():
-        F.linear(x2, w_qkv, out=y)
-        ctx.fused_qk_norm_rope_scatter(yq, yk, w_q, w_k, cos, sin, eps=w.eps, v=yv, tags=("pq", "pk", "pv"))
-        ctx.wait()
-        ctx.gather_out(o)
+        def step_per_operator(x2=x.view(M, hidden), y=y, yq=yq, yk=yk, yv=yv, o=o, outs=outs, z=z):
+            F.linear(x2, w_qkv, out=y)
+            ctx.fused_qk_norm_rope_scatter(yq, yk, w_q, w_k, cos, sin, eps=w.eps, v=yv, out=outs)
+            ctx.wait()
+            ctx.gather_out(o, out=z)
 
-    return {"workload": w, "name": name, "ctx": ctx, "step": step,
-            "step_per_operator": step_per_operator,
+        steps.append(step)
+        per_op.append(step_per_operator)
+    return {"workload": w, "name": name, "ctx": ctx, "steps": steps, "per_operator": per_op,
             "bytes_per_step": flops, "unit": "TFLOP/s", "unit_div": 1e12,
             "metric": "QKV projection + QK-norm + RoPE + Ulysses scatter + output gather, projection TFLOP/s "
                       "over the step, P=%d bf16, 1 MI355X" % P,
             "dominant": ("proj", flops, "proj_kernel<bf16> (MFMA QKV projection with norm/RoPE/band-store "
                          "epilogue)", "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"),
-            "cpu_proj": (x, w_qkv, w_q, w_k, Hq, Hkv, w.eps, w.theta),
+            "cpu_proj": (x0, w_qkv, w_q, w_k, Hq, Hkv, w.eps, w.theta),
             "dtype": "bf16", "data": "synthetic N(0,1) activations, N(0,1/hidden) QKV weight, N(1,0.1) norm "
                                      "weights, 1-D RoPE theta 1e4 (seeded)",
             "config": {"workload": name, "P": P, "B": B, "S_local": S_l, "S": P * S_l, "Hq": Hq, "Hkv": Hkv,
@@ -322,14 +390,14 @@ def _setup_proj(torch, dev, synth, rope_table_1d, UlyssesContext, w, seed, name)
                        "parallelism": "ulysses-p%d-emulated" % P}}
 
 
-def setup_video_dit_proj(torch, dev, synth, rope_table_1d, UlyssesContext):
+def setup_video_dit_proj(torch, dev, synth, rope_table_1d, UlyssesContext, sets=3):
     return _setup_proj(torch, dev, synth, rope_table_1d, UlyssesContext, synth.VIDEO_DIT, 70,
-                       "video_dit_proj_p4_s16384_h24_hidden3072_bf16")
+                       "video_dit_proj_p4_s16384_h24_hidden3072_bf16", sets)
 
 
-def setup_gqa_proj(torch, dev, synth, rope_table_1d, UlyssesContext):
+def setup_gqa_proj(torch, dev, synth, rope_table_1d, UlyssesContext, sets=3):
     return _setup_proj(torch, dev, synth, rope_table_1d, UlyssesContext, synth.GQA, 80,
-                       "gqa_proj_p8_b2_s65536_hq32_hkv8_hidden4096_bf16")
+                       "gqa_proj_p8_b2_s65536_hq32_hkv8_hidden4096_bf16", sets)
 
 
 def cpu_baseline_proj(args, proj_inputs, min_seconds: float = 10.0):
@@ -367,62 +435,145 @@ WORKLOADS = {"video_dit": setup_video_dit, "wan_long": setup_wan_long, "gqa": se
              "spatial": setup_spatial, "video_dit_proj": setup_video_dit_proj, "gqa_proj": setup_gqa_proj}
 
 
-def measure_protocol(args, torch, dev, setup, step, timed, samples: int = 100):
-    """The rest of the timing protocol, outside the timed region: the spread
-    of single steps (events on the stream every kernel of the step runs on),
-    an A/A repeat of the timed loop, a plain device copy of the step's bytes
-    (torch's, and the library's own relayout kernel as an identity copy: the
-    copy roof of this box), and the same step in fp16 (a relayout moves bytes,
-    so the rate must not depend on the 16-bit type)."""
+def pick(sorted_vals, q):
+    """The q-quantile of an ascending list (nearest rank)."""
+    return sorted_vals[min(len(sorted_vals) - 1, int(q * len(sorted_vals)))]
+
+
+class FenceFreeEvents:
+    """HIP timing events created with hipEventDisableSystemFence, recorded on the
+    current stream.  A default event's system-scope release writes the L2 back
+    each time it is recorded; between back-to-back steps that would add work a
+    real pipeline does not have.  HIP is reached through the runtime torch has
+    already loaded (measurement plumbing only)."""
+    FLAGS = 0x20000000       # hipEventDisableSystemFence
+
+    def __init__(self, torch, n):
+        import ctypes
+        self.torch = torch
+        self.hip = ctypes.CDLL("libamdhip64.so.7", mode=ctypes.RTLD_GLOBAL)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.FLAGS) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+        self._c = ctypes
+
+    def record(self, i):
+        st = self.torch.cuda.current_stream().cuda_stream
+        if self.hip.hipEventRecord(self.ev[i], self._c.c_void_p(st)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed(self, i, j):
+        ms = self._c.c_float()
+        if self.hip.hipEventElapsedTime(self._c.byref(ms), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
+def back_to_back(torch, fns, n):
+    """Run n steps back to back, step i on input/output set i % len(fns), with
+    a fence-free HIP event on the current stream before every step and after the last:
+    step i's time is the interval between its event and the next one, so the
+    work a step leaves behind (a write-back still under way, say) is charged
+    to the steps, and the host enqueues ahead of the GPU without waiting.
+    Returns the sorted per-step times (ms), the sorted host enqueue times per
+    step (s) and the events' total over the n steps (ms)."""
+    ev = FenceFreeEvents(torch, n + 1)
+    host = []
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev.record(i)
+        h0 = time.perf_counter()
+        fns[i % len(fns)]()
+        host.append(time.perf_counter() - h0)
+    ev.record(n)
+    torch.cuda.synchronize()
+    times = sorted(ev.elapsed(i, i + 1) for i in range(n))
+    total = ev.elapsed(0, n)
+    ev.close()
+    return times, sorted(host), total
+
+
+def cold_steps(torch, fn, n, scrub):
+    """Run `fn` n times, each after a read of the 1 GiB `scrub` buffer (which
+    evicts the L2s and the Infinity Cache), with HIP events around the step
+    alone.  Unlike `back_to_back`, whatever a step leaves in the caches to be
+    written back is written back during the next scrub, outside the events."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        scrub.max()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+
+
+def spread(times_ms, work, unit_div, unit):
+    """Median, p10 and p90 of per-step times, and the rate at the median."""
+    med = pick(times_ms, 0.5)
+    return {"samples": len(times_ms), "median_us": round(med * 1e3, 2),
+            "p10_us": round(pick(times_ms, 0.1) * 1e3, 2), "p90_us": round(pick(times_ms, 0.9) * 1e3, 2),
+            unit.replace("/", "_") + "_at_median": round(work / (med * 1e-3) / unit_div, 2)}
+
+
+def measure_protocol(args, torch, dev, setup, headline_gbs):
+    """Controls beside the headline, timed the same way (back to back over
+    rotating buffer sets): a device copy of the step's bytes by torch, the same
+    bytes through the library's own relayout kernel as an identity copy (this
+    box's copy roof), and the same step in fp16 (a relayout moves bytes, so the
+    rate must not depend on the 16-bit type)."""
     from sequence_attention_ulysses_amd import UlyssesContext, rope_table_1d, synth
 
     nbytes = setup["bytes_per_step"]
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
-    for e0, e1 in ev:
-        e0.record()
-        step()
-        e1.record()
-    torch.cuda.synchronize()
-    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
-    pick = lambda q: t[min(len(t) - 1, int(q * len(t)))]
-    spread = {"samples": samples, "median_us": round(pick(0.5) * 1e3, 2), "p10_us": round(pick(0.1) * 1e3, 2),
-              "p90_us": round(pick(0.9) * 1e3, 2), "GB_s_at_median": round(nbytes / (pick(0.5) * 1e-3) / 1e9, 1)}
+    n = max(MIN_TIMED_LAUNCHES, args.steps)
+    R = len(setup["steps"])
 
-    wall = timed(step, args.steps)
-    aa = {"ms_per_step": round(wall * 1e3 / args.steps, 5), "GB_s": round(nbytes / (wall / args.steps) / 1e9, 2)}
+    pairs = [(torch.empty(nbytes // 2, dtype=torch.uint8, device=dev).fill_(1),
+              torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)) for _ in range(R)]
+    t, _, _ = back_to_back(torch, [lambda s=s, d=d: d.copy_(s) for s, d in pairs], n)
+    copy = {"bytes_copied": nbytes // 2, "median_us": round(pick(t, 0.5) * 1e3, 2),
+            "GB_s": round(nbytes / (pick(t, 0.5) * 1e-3) / 1e9, 1)}
+    del pairs
 
-    # a device-to-device copy moving the same bytes (half read, half written)
-    src = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    wall = timed(lambda: dst.copy_(src), args.steps)
-    copy = {"bytes_copied": nbytes // 2, "ms": round(wall * 1e3 / args.steps, 5),
-            "GB_s": round(nbytes / (wall / args.steps) / 1e9, 2)}
-    del src, dst
-
-    # the same bytes through the library's own relayout kernel as a plain copy
-    # (one rank: the identity map), on the caller's stream: this box's copy roof
+    # the same bytes through the library's relayout kernel as a plain copy (one
+    # rank: the identity map) on the caller's stream
     rows = (nbytes // 2) // (128 * 128 * 2)
-    csrc = torch.ones((1, 1, rows, 128, 128), dtype=torch.bfloat16, device=dev)
-    cdst = torch.empty_like(csrc)
+    pairs = [(torch.ones((1, 1, rows, 128, 128), dtype=torch.bfloat16, device=dev),
+              torch.empty((1, 1, rows, 128, 128), dtype=torch.bfloat16, device=dev)) for _ in range(R)]
     with UlyssesContext(1, device=0) as cctx:
         cctx.set_route("caller")
-        for _ in range(args.warmup):
-            cctx.scatter_qkv(q=csrc, out=(cdst, None, None))
-        wall = timed(lambda: cctx.scatter_qkv(q=csrc, out=(cdst, None, None)), args.steps)
-    cbytes = 2 * csrc.numel() * 2
+        fns = [lambda s=s, d=d: cctx.scatter_qkv(q=s, out=(d, None, None)) for s, d in pairs]
+        for i in range(max(args.warmup, R)):
+            fns[i % R]()
+        t, _, _ = back_to_back(torch, fns, n)
+    cbytes = 2 * pairs[0][0].numel() * 2
     copy_roof = {"kernel": "relayout_kernel, one rank (identity map)", "bytes_moved": cbytes,
-                 "us": round(wall * 1e6 / args.steps, 2), "GB_s": round(cbytes / (wall / args.steps) / 1e9, 1)}
-    del csrc, cdst
+                 "median_us": round(pick(t, 0.5) * 1e3, 2),
+                 "GB_s": round(cbytes / (pick(t, 0.5) * 1e-3) / 1e9, 1)}
+    copy_roof["step_over_copy_roof"] = round(headline_gbs / copy_roof["GB_s"], 4)
+    del pairs
 
-    f16 = setup_video_dit(torch, dev, synth, rope_table_1d, UlyssesContext, dtype="f16")
-    for _ in range(args.warmup):
-        f16["step"]()
-    wall = timed(f16["step"], args.steps)
+    f16 = setup_video_dit(torch, dev, synth, rope_table_1d, UlyssesContext, sets=R, dtype="f16")
+    for i in range(max(args.warmup, R)):
+        f16["steps"][i % R]()
+    t, _, _ = back_to_back(torch, f16["steps"], n)
     f16["ctx"].close()
-    fp16 = {"ms_per_step": round(wall * 1e3 / args.steps, 5), "GB_s": round(nbytes / (wall / args.steps) / 1e9, 2)}
-    copy_roof["step_over_copy_roof"] = round(aa["GB_s"] / copy_roof["GB_s"], 4)
-    return {"step_spread": spread, "aa_repeat": aa, "device_copy_control": copy, "copy_roof": copy_roof,
-            "fp16_same_shape": fp16}
+    del f16
+    fp16 = spread(t, nbytes, 1e9, "GB/s")
+    return {"device_copy_control": copy, "copy_roof": copy_roof, "fp16_same_shape": fp16}
 
 
 def calibrate_copy(args, torch, UlyssesContext):
@@ -450,14 +601,20 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time each step after a 1 GiB read that evicts the caches (event-timed, reported apart)")
+    ap.add_argument("--sets", type=int, default=3,
+                    help="independent input/output buffer sets the timed steps rotate over (1: every step reuses "
+                         "the same buffers, so data stays in the caches between steps)")
     ap.add_argument("--no-profile", action="store_true", help="do not bracket launches with timing events")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="run the warmup and the headline steps only (for counter collection); the record is "
+                         "marked invalid")
     ap.add_argument("--graph", action="store_true",
-                    help="capture one step into a HIP graph and time its replays (no per-launch host work; "
-                         "implies --no-profile and --no-two-stream)")
-    ap.add_argument("--no-two-stream", action="store_true",
-                    help="skip the two-stream comparison (profiling runs then hold only the headline step)")
+                    help="capture one step per buffer set into a HIP graph and time their replays (no per-launch "
+                         "host work; implies --no-profile)")
+    ap.add_argument("--two-stream", action="store_true",
+                    help="also time the two-stream form of step 1 (V scattered on the library's comm stream beside "
+                         "the fused Q/K launch); off by default so that every fused launch of the run is the same "
+                         "launch and a kernel trace of the run averages that launch alone")
     ap.add_argument("--route", choices=("kernel", "copy_engine", "caller"), default=None,
                     help="how the plain Q/K/V scatter moves its operands (the library default: kernel on the "
                          "comm stream); the workloads that use it are gqa and tiny")
@@ -480,152 +637,151 @@ def main():
         return
 
     dev = torch.device("cuda", 0)
-    setup = WORKLOADS[args.workload](torch, dev, synth, rope_table_1d, UlyssesContext)
+    setup = WORKLOADS[args.workload](torch, dev, synth, rope_table_1d, UlyssesContext, sets=args.sets)
     w = setup["workload"]
     ctx = setup["ctx"]
     if args.route:
         ctx.set_route(args.route)
         setup["config"]["scatter_route"] = args.route
-    step, step_two_stream = setup["step"], setup.get("step_two_stream")
-    step_per_operator = setup.get("step_per_operator")
+    steps, steps_two_stream = setup["steps"], setup.get("two_stream")
+    steps_per_operator = setup.get("per_operator")
+    R = len(steps)
     args.bytes_per_step = setup["bytes_per_step"]        # the step's work: bytes, or flops for TFLOP/s
     unit, unit_div = setup.get("unit", "GB/s"), setup.get("unit_div", 1e9)
     name = setup.get("name", w.name)
-    if step_two_stream is None:
-        args.no_two_stream = True
-    print("bench: %s on %s, %d warmup + %d timed steps" % (name, torch.cuda.get_device_name(0),
-                                                         args.warmup, args.steps), file=sys.stderr, flush=True)
+    args.no_two_stream = steps_two_stream is None or not args.two_stream
+    print("bench: %s on %s, %d warmup + %d timed steps over %d buffer sets" % (
+        name, torch.cuda.get_device_name(0), args.warmup, args.steps, R), file=sys.stderr, flush=True)
 
-    def timed(fn, steps):
+    def timed(fn, n):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
+        for _ in range(n):
             fn()
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
     if args.graph:
         args.no_profile = args.no_two_stream = True
-        step_per_operator = None
-    for _ in range(args.warmup):
-        step()
+        steps_per_operator = None
+    for i in range(max(args.warmup, R)):
+        steps[i % R]()
         if not args.no_two_stream:
-            step_two_stream()
-        if step_per_operator is not None:
-            step_per_operator()
+            steps_two_stream[i % R]()
+        if steps_per_operator is not None:
+            steps_per_operator[i % R]()
     torch.cuda.synchronize()
     if args.graph:
-        # the library's calls are capturable: its targets are registered and its
-        # event pools filled by the warmup steps, and a step allocates nothing
+        # the library's calls are capturable: a step with explicit destinations
+        # allocates nothing, and the warmup filled the context's event pools
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            step()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=cap):
-            step()
-        torch.cuda.synchronize()
-        step = graph.replay
-        for _ in range(args.warmup):
-            step()
+        graphs = []
+        for fn in steps:
+            with torch.cuda.stream(cap):
+                fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                fn()
+            torch.cuda.synchronize()
+            graphs.append(g)
+        steps = [g.replay for g in graphs]
+        for i in range(max(args.warmup, R)):
+            steps[i % R]()
         torch.cuda.synchronize()
         setup["config"]["launch"] = "hip_graph"
     dom_kind, dom_bytes, dom_name = setup["dominant"][:3]
     dom_bound, dom_peak, dom_unit = (setup["dominant"][3:] if len(setup["dominant"]) > 3
                                      else ("hbm", HBM_PEAK_GBS, "GB/s"))
-    if not args.no_profile:
-        # time only the dominant kernel, one launch in PROFILE_EVERY: every event pair adds
-        # latency between kernels
-        ctx.profile(True, kinds=[dom_kind], every=PROFILE_EVERY)
-        ctx.profile_reset()
-    wall = timed(step, args.steps)
-    ms_per_step = wall * 1e3 / args.steps
-    value = args.bytes_per_step / (wall / args.steps) / unit_div
+    work = args.bytes_per_step
+    ukey = unit.replace("/", "_")
 
+    # the headline: exactly --steps steps back to back over the rotating sets
+    t_a, host_a, total_a = back_to_back(torch, steps, args.steps)
+    med = pick(t_a, 0.5)
+    ms_per_step = med
+    value = work / (med * 1e-3) / unit_div
+    headline = spread(t_a, work, unit_div, unit)
+    headline["mean_us"] = round(total_a * 1e3 / args.steps, 2)
+    host_us = pick(host_a, 0.5) * 1e6
+    host = {"median_us": round(host_us, 2), "p90_us": round(pick(host_a, 0.9) * 1e6, 2),
+            "frac_of_step": round(host_us / (med * 1e3), 3)}
+
+    invalid = []
+    if args.headline_only:
+        # counter runs: the warmup and the headline steps alone
+        args.no_profile = args.no_two_stream = True
+        steps_per_operator = None
+        invalid.append("headline steps only (a counter-collection run)")
+        aa = None
+    else:
+        # A/A control: the same measurement again; a drift over 2 % voids the record
+        t_b, _, _ = back_to_back(torch, steps, args.steps)
+        drift = pick(t_b, 0.5) / med - 1.0
+        aa = dict(spread(t_b, work, unit_div, unit), drift=round(drift, 4))
+        if abs(drift) > AA_MAX_DRIFT:
+            invalid.append("A/A repeat drifted %+.1f %% (limit %.0f %%)" % (100 * drift, 100 * AA_MAX_DRIFT))
+
+    # every kernel of at least 10 steps bracketed by the library's own events on
+    # the stream it runs on: the dominant kernel's average is the roofline figure
     kernels = {}
     roofline = None
     if not args.no_profile:
-        ms, n = ctx.profile_read(dom_kind)
-        if n:
-            avg_us = ms * 1e3 / n
-            div = 1e9 if dom_unit == "GB/s" else 1e12
-            kernels[dom_kind] = {"timed_launches": n, "launches": args.steps, "avg_us": round(avg_us, 2),
-                                 "work_per_launch": dom_bytes,
-                                 dom_unit.replace("/", "_"): round(dom_bytes / (avg_us * 1e-6) / div, 1)}
+        n_dom = max(MIN_TIMED_LAUNCHES, args.steps)
+        ctx.profile(True, every=1)
+        ctx.profile_reset()
+        back_to_back(torch, steps, n_dom)
+        from sequence_attention_ulysses_amd._lib import KERNEL_KINDS
+        for kind in KERNEL_KINDS:
+            ms, n = ctx.profile_read(kind)
+            if n:
+                kernels[kind] = {"timed_launches": n, "avg_us": round(ms * 1e3 / n, 2)}
         ctx.profile(False)
         ctx.profile_reset()
         dom = kernels.get(dom_kind)
+        if dom is None or dom["timed_launches"] < MIN_TIMED_LAUNCHES:
+            invalid.append("fewer than %d timed launches of the dominant kernel" % MIN_TIMED_LAUNCHES)
         if dom:
-            achieved = dom[dom_unit.replace("/", "_")]
+            div = 1e9 if dom_unit == "GB/s" else 1e12
+            achieved = round(dom_bytes / (dom["avg_us"] * 1e-6) / div, 1)
+            dom.update(work_per_launch=dom_bytes, **{dom_unit.replace("/", "_"): achieved})
             roofline = {"bound": dom_bound, "achieved": achieved, "peak": dom_peak, "unit": dom_unit,
                         "frac": round(achieved / dom_peak, 4),
                         "traffic": traffic_from_profiles(name) if dom_bound == "hbm" else None,
-                        "kernel": dom_name, "avg_us": dom["avg_us"],
+                        "kernel": dom_name, "avg_us": dom["avg_us"], "timed_launches": dom["timed_launches"],
                         ("algorithmic_bytes_per_launch" if dom_bound == "hbm" else "flops_per_launch"): dom_bytes}
 
-    # the two-stream form of the same step, timed the same way (no events)
-    two_stream = None
-    if not args.no_two_stream:
-        wall2 = timed(step_two_stream, args.steps)
-        two_stream = {"ms_per_step": round(wall2 * 1e3 / args.steps, 5),
-                      "GB_s": round(args.bytes_per_step / (wall2 / args.steps) / 1e9, 2)}
-
-    per_operator = None
-    if step_per_operator is not None:
-        wall3 = timed(step_per_operator, args.steps)
-        per_operator = {"path": "torch linear (hipBLASLt) writing qkv, then fused_qk_norm_rope_scatter, wait, gather",
-                        "ms_per_step": round(wall3 * 1e3 / args.steps, 5),
-                        unit.replace("/", "_"): round(args.bytes_per_step / (wall3 / args.steps) / unit_div, 2),
-                        "fused_speedup": round(wall3 / wall, 4)}
-
-    cold = None
-    if args.cold:
-        # Reading 1 GiB evicts the L2s and the 256 MB Infinity Cache without
-        # leaving dirty lines whose write-back would overlap the timed step.
+    # cross-checks: a wall-clock loop on one set (its data stays warm in the
+    # caches between steps), and each step after a 1 GiB cache-evicting read
+    warm = scrub_cold = None
+    if not args.headline_only:
+        wall_w = timed(steps[0], args.steps)
+        warm = {"ms_per_step": round(wall_w * 1e3 / args.steps, 5),
+                ukey: round(work / (wall_w / args.steps) / unit_div, 2)}
         scrub = torch.ones(1 << 27, dtype=torch.int64, device=dev)
-        torch.cuda.synchronize()
-        times = []
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(20):
-            # no wait between the scrub and the step: the host enqueues the
-            # step while the scrub runs, so the events time the GPU, not the
-            # host's launch latency
-            scrub.max()
-            e0.record()
-            step()
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        times.sort()
-        med = times[len(times) // 2]
-        cold = {"median_ms": round(med, 4),
-                unit.replace("/", "_"): round(args.bytes_per_step / (med * 1e-3) / unit_div, 1),
-                "p10_ms": round(times[2], 4), "p90_ms": round(times[17], 4)}
-        # the same cold steps again, each kernel bracketed by the library's own events
-        if not args.no_profile:
-            ctx.profile(True, every=1)
-            ctx.profile_reset()
-            for _ in range(20):
-                scrub.max()
-                torch.cuda.synchronize()
-                step()
-                torch.cuda.synchronize()
-            per_kernel = {}
-            from sequence_attention_ulysses_amd._lib import KERNEL_KINDS
-            for kind in KERNEL_KINDS:
-                ms, n = ctx.profile_read(kind)
-                if n:
-                    per_kernel[kind] = round(ms * 1e3 / n, 2)
-            ctx.profile(False)
-            ctx.profile_reset()
-            cold["kernel_avg_us"] = per_kernel
+        scrub_cold = spread(cold_steps(torch, steps[0], max(MIN_TIMED_LAUNCHES, args.steps), scrub), work,
+                            unit_div, unit)
         del scrub
 
-    extra = (measure_protocol(args, torch, dev, setup, step, timed)
-             if args.workload == "video_dit" and not args.graph else None)
+    # the two-stream form of the same step, timed like the headline
+    two_stream = None
+    if not args.no_two_stream:
+        t2, _, _ = back_to_back(torch, steps_two_stream, args.steps)
+        two_stream = spread(t2, work, unit_div, unit)
+
+    per_operator = None
+    if steps_per_operator is not None:
+        t3, _, _ = back_to_back(torch, steps_per_operator, args.steps)
+        per_operator = dict(spread(t3, work, unit_div, unit),
+                            path="torch linear (hipBLASLt) writing qkv, then fused_qk_norm_rope_scatter, wait, gather",
+                            fused_speedup=round(pick(t3, 0.5) / med, 4))
 
     ctx.close()
+    del steps, steps_two_stream, steps_per_operator
+    setup.pop("steps", None), setup.pop("two_stream", None), setup.pop("per_operator", None)
+    extra = (measure_protocol(args, torch, dev, dict(setup, steps=[None] * R), work / (med * 1e-3) / 1e9)
+             if args.workload == "video_dit" and not (args.graph or args.headline_only) else None)
 
     cpu = None
     if not args.no_cpu_baseline and "cpu_inputs" in setup:
@@ -651,16 +807,24 @@ def main():
         "data": setup["data"],
         "config": setup["config"],
         "roofline": roofline,
-        "kernels": kernels,
-        "two_stream": two_stream,
         "cpu_baseline": cpu,
+        "valid": not invalid,
+        "timing": "median of %d steps run back to back over %d rotating input/output sets (no data a step "
+                  "reads is cached from the step before), HIP events between the steps" % (args.steps, R),
+        "step_spread": headline,
+        "aa_repeat": aa,
+        "host_enqueue": host,
+        "kernels": kernels,
+        "warm_loop": warm,
+        "scrub_cold": scrub_cold,
+        "two_stream": two_stream,
     }
+    if invalid:
+        rec["invalid_reason"] = "; ".join(invalid)
     if unit == "GB/s":
         rec["hbm_frac"] = round(value / HBM_PEAK_GBS, 4)
     if per_operator:
         rec["per_operator"] = per_operator
-    if cold:
-        rec["cold_cache"] = cold
     if extra:
         rec.update(extra)
     print(json.dumps(rec), flush=True)

@@ -70,6 +70,10 @@ struct NormRopeArgs {
     uint32_t D;
     float eps;
     float inv_D;
+    // operand-major band form: block row k of the grid's operand-major order
+    // belongs to operand task_op[k] (the operands present, in order)
+    uint32_t P;
+    uint32_t task_op[3];
 };
 
 // ---------------------------------------------------------------------------
@@ -105,10 +109,10 @@ struct RowMapArgs {
 
 // Launch wrappers (uly_kernels.hip).  They only enqueue; the caller checks
 // hipGetLastError().
-// system_scope: the cache-resident gather policy (kGather*), else kScatter*.
-void launch_relayout(const CopyBatch &b, bool system_scope, hipStream_t stream);
+void launch_relayout(const CopyBatch &b, hipStream_t stream);
 void launch_norm_rope(const NormRopeArgs &a, int lanes, int dtype, bool uniform, bool tile, uint32_t blocks,
                       hipStream_t stream);
+void launch_norm_rope_band(const NormRopeArgs &a, int dtype, uint32_t blocks, hipStream_t stream);
 void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
 
 #ifndef ULY_THREADS
@@ -126,23 +130,26 @@ void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
 #ifndef ULY_ROPE_THREADS
 #define ULY_ROPE_THREADS 768
 #endif
+#ifndef ULY_BAND_WAVES
+#define ULY_BAND_WAVES 4
+#endif
+#ifndef ULY_BAND_TOKENS
+#define ULY_BAND_TOKENS 2
+#endif
+#ifndef ULY_BAND_INFLIGHT
+#define ULY_BAND_INFLIGHT 5
+#endif
 #ifndef ULY_RELAYOUT_NT_LOAD
 #define ULY_RELAYOUT_NT_LOAD 1
 #endif
 #ifndef ULY_RELAYOUT_NT_STORE
 #define ULY_RELAYOUT_NT_STORE 1
 #endif
-#ifndef ULY_SCATTER_LOAD
-#define ULY_SCATTER_LOAD 1
+#ifndef ULY_EXCHANGE_LOAD
+#define ULY_EXCHANGE_LOAD 1
 #endif
-#ifndef ULY_SCATTER_STORE
-#define ULY_SCATTER_STORE 1
-#endif
-#ifndef ULY_GATHER_LOAD
-#define ULY_GATHER_LOAD 2
-#endif
-#ifndef ULY_GATHER_STORE
-#define ULY_GATHER_STORE 2
+#ifndef ULY_EXCHANGE_STORE
+#define ULY_EXCHANGE_STORE 2
 #endif
 #ifndef ULY_ROPE_NT_LOAD
 #define ULY_ROPE_NT_LOAD 1
@@ -154,12 +161,10 @@ void launch_rowmap(const RowMapArgs &a, int kind, hipStream_t stream);
 // 1 non-temporal (streaming), 2 system scope.
 constexpr int kRelayoutNtLoad = ULY_RELAYOUT_NT_LOAD;     // row maps (pad/trim, spatial)
 constexpr int kRelayoutNtStore = ULY_RELAYOUT_NT_STORE;
-constexpr int kScatterLoad = ULY_SCATTER_LOAD;             // Q/K/V scatter, chunk exchange
-constexpr int kScatterStore = ULY_SCATTER_STORE;
-constexpr int kGatherLoad = ULY_GATHER_LOAD;               // output gather within the Infinity Cache
-constexpr int kGatherStore = ULY_GATHER_STORE;
-// A gather whose input + output bytes fit in the 256 MB Infinity Cache uses
-// the system-scope policy; larger gathers stream with the scatter policy.
+constexpr int kExchangeLoad = ULY_EXCHANGE_LOAD;           // scatter, gather and chunk exchange
+constexpr int kExchangeStore = ULY_EXCHANGE_STORE;
+// Operands beyond the 256 MB Infinity Cache stream from HBM (the projection
+// picks its deeper token ring for them).
 constexpr int64_t kCacheResidentBytes = int64_t(256) << 20;
 constexpr int kRopeNtLoad = ULY_ROPE_NT_LOAD;
 constexpr int kRopeNtStore = ULY_ROPE_NT_STORE;
@@ -169,5 +174,8 @@ constexpr uint32_t kCopyVecsPerBlock = kThreads * kCopyUnroll;
 constexpr int kRopeTokens = ULY_ROPE_TOKENS;            // tokens per block
 constexpr int kRopeSlots = ULY_ROPE_SLOTS;              // head slots a lane group loads at once
 constexpr int kRopeThreads = ULY_ROPE_THREADS;          // threads per block of the fused kernel
+constexpr int kBandWaves = ULY_BAND_WAVES;              // waves per block of the operand-major band form
+constexpr int kBandTokens = ULY_BAND_TOKENS;            // tokens per block there
+constexpr int kBandInflight = ULY_BAND_INFLIGHT;        // row loads a lane keeps in flight there
 
 }  // namespace uly

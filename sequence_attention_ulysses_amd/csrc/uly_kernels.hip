@@ -31,15 +31,15 @@ typedef __attribute__((address_space(1))) u32x4 global_u32x4;
 // All operands live in device (global) memory: the explicit address space
 // keeps the accesses global_load/store instead of flat ones.  Operand data
 // streams through exactly once; each kernel picks the cache policy of its
-// loads and of its stores (uly_internal.h).  Measured on the video-DiT step:
-// a gather whose input and output fit in the 256 MB Infinity Cache runs
-// fastest with system-scope accesses (sc0 sc1, through a volatile access:
-// video-DiT output gather 35.8 -> 31.0 us), larger gathers and the scatters
-// with non-temporal ones (system scope there: GQA Q/K/V scatter 527 -> 553
-// us, GQA and Wan gathers 2 % slower),
-// and the fused norm + RoPE kernel with non-temporal ones too (system scope:
-// 107 -> 133 us, since a volatile access is followed by a wait and the
-// kernel keeps four loads per thread in flight).
+// loads and of its stores (uly_internal.h).  Measured with steps run back to
+// back over rotating buffer sets (so every byte a step writes is charged to
+// the steps): the exchange kernels (scatter, gather, chunk exchange) run
+// fastest with non-temporal loads and system-scope stores (video-DiT output
+// gather 37.1 -> 32.8 us, GQA Q/K/V scatter 525 -> 506 us against
+// non-temporal or system-scope accesses on both sides), the fused norm + RoPE
+// kernels with non-temporal loads and stores (ordinary or system-scope
+// stores finish the fused launch sooner, 98 us against 104, but leave
+// write-back that the next launch pays for: step 150-155 us against 139).
 // Policy 0: ordinary access; 1: non-temporal (nt); 2: system scope (sc0 sc1,
 // through a volatile access).
 template <int POL>
@@ -357,6 +357,96 @@ __global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_ker
     }
 }
 
+// Operand-major band form, for operands that are each one dense tensor
+// (Q, K and V not interleaved in a fused projection).  A block owns one
+// operand of a tile of kBandTokens consecutive tokens of one rank and batch
+// (S_l a multiple of the tile); the grid runs operand by operand, so the
+// blocks in flight read one operand's tensor front to back and write only
+// its P destination bands.  Each wave owns one destination rank q at a time:
+// the Hl head rows of band q for every token of the tile, which are one
+// contiguous run of the destination (Hl * tokens * D elements).  The wave
+// walks the run four rows at a time (one per 16-lane group), so every store
+// instruction writes 1 KiB of consecutive destination bytes.  D = 128
+// (16 lanes per row).
+template <int DT>
+__global__ __launch_bounds__(kBandWaves * 64) void norm_rope_band_kernel(NormRopeArgs a) {
+    constexpr int LANES = 16, GPW = 64 / LANES, TU = kBandTokens, MAXT = kBandInflight;
+    const uint32_t lane = threadIdx.x % LANES;
+    const uint32_t gi = (threadIdx.x % 64) / LANES;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const uint32_t ntiles = a.tokens / TU;
+    const uint32_t lb = logical_block(blockIdx.x, gridDim.x);
+    const uint32_t op_slot = lb / ntiles;                    // block-uniform
+    const uint32_t tk0 = (lb - op_slot * ntiles) * TU;
+    const uint32_t oi = sel3(op_slot, a.task_op[0], a.task_op[1], a.task_op[2]);
+    uint32_t rb, s0, r, b;
+    a.sl.divmod(tk0, rb, s0);
+    a.bdiv.divmod(rb, r, b);
+    const uint32_t g0 = r * a.S_l + s0;
+    // this lane's cos/sin of every token of the tile
+    float4 cs[TU], sn[TU];
+    const bool rope = oi < 2;                                // a V block rotates nothing: no table row
+#pragma unroll
+    for (int t = 0; t < TU; ++t) {
+        const size_t t_off = size_t(g0 + t) * (a.D / 2) + lane * 4;
+        cs[t] = rope ? load_table4(a.cos_tab + t_off) : make_float4(1.f, 1.f, 1.f, 1.f);
+        sn[t] = rope ? load_table4(a.sin_tab + t_off) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (uint32_t q = wave; q < a.P; q += kBandWaves) {
+        const NormRopeOperand &o0 = a.op[0], &o1 = a.op[1], &o2 = a.op[2];
+        const FastDiv hl = oi == 0 ? o0.hl : (oi == 1 ? o1.hl : o2.hl);
+        const uint32_t Hl = hl.d;
+        const uint32_t rows = Hl * TU;
+        const int64_t s_s = sel3(oi, o0.s_s, o1.s_s, o2.s_s), s_h = sel3(oi, o0.s_h, o1.s_h, o2.s_h);
+        const int64_t d_g = sel3(oi, o0.d_g, o1.d_g, o2.d_g), d_j = sel3(oi, o0.d_j, o1.d_j, o2.d_j);
+        const uint16_t *src = sel3(oi, o0.src, o1.src, o2.src) + int64_t(r) * sel3(oi, o0.s_rank, o1.s_rank, o2.s_rank) +
+                              int64_t(b) * sel3(oi, o0.s_b, o1.s_b, o2.s_b) + int64_t(s0) * s_s +
+                              int64_t(q) * Hl * s_h + lane * 8;
+        uint16_t *dst = sel3(oi, o0.dst, o1.dst, o2.dst) + int64_t(q) * sel3(oi, o0.d_q, o1.d_q, o2.d_q) +
+                        int64_t(b) * sel3(oi, o0.d_b, o1.d_b, o2.d_b) + int64_t(g0) * d_g + lane * 8;
+        const uint4 wraw = load16_cached(sel3(oi, o0.w, o1.w, o2.w) + lane * 8);
+        for (uint32_t k0 = 0; k0 < rows; k0 += GPW * MAXT) {
+            uint4 raw[MAXT];
+            uint32_t tt[MAXT], jj[MAXT];
+#pragma unroll
+            for (int u = 0; u < MAXT; ++u) {
+                const uint32_t k = min(k0 + u * GPW + gi, rows - 1);
+                hl.divmod(k, tt[u], jj[u]);
+                raw[u] = load16<kRopeNtLoad>(src + int64_t(tt[u]) * s_s + int64_t(jj[u]) * s_h);
+            }
+            float w[8];
+            unpack8<DT>(wraw, w);
+#pragma unroll
+            for (int u = 0; u < MAXT; ++u) {
+                const uint32_t k = k0 + u * GPW + gi;
+                float x[8];
+                unpack8<DT>(raw[u], x);
+                float ss = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+                ss = row_sum<LANES>(ss);
+                // eps > 0 keeps the argument normal: the bare reciprocal square root suffices
+                const float inv = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_D, a.eps));
+                float4 c4 = cs[0], s4 = sn[0];
+#pragma unroll
+                for (int t = 1; t < TU; ++t)
+                    if (tt[u] == uint32_t(t)) { c4 = cs[t]; s4 = sn[t]; }
+                const float c[4] = {c4.x, c4.y, c4.z, c4.w};
+                const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+                uint32_t out[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float n0 = x[2 * p] * inv * w[2 * p];
+                    const float n1 = x[2 * p + 1] * inv * w[2 * p + 1];
+                    out[p] = pack2<DT>(n0 * c[p] - n1 * sv[p], n0 * sv[p] + n1 * c[p]);
+                }
+                const uint4 res = rope ? make_uint4(out[0], out[1], out[2], out[3]) : raw[u];
+                if (k < rows) store16<kRopeNtStore>(dst + int64_t(tt[u]) * d_g + int64_t(jj[u]) * d_j, res);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Row maps with zero fill: sequence pad/trim (parallel_shard.py's role in
 // "Communication Architecture") and height shards with halos, the
@@ -430,12 +520,8 @@ __global__ __launch_bounds__(kThreads) void rowmap_kernel(RowMapArgs a) {
 
 }  // namespace
 
-void launch_relayout(const CopyBatch &b, bool system_scope, hipStream_t stream) {
-    if (system_scope)
-        hipLaunchKernelGGL((relayout_kernel<kGatherLoad, kGatherStore>), dim3(b.blocks), dim3(kThreads), 0, stream, b);
-    else
-        hipLaunchKernelGGL((relayout_kernel<kScatterLoad, kScatterStore>), dim3(b.blocks), dim3(kThreads), 0, stream,
-                           b);
+void launch_relayout(const CopyBatch &b, hipStream_t stream) {
+    hipLaunchKernelGGL((relayout_kernel<kExchangeLoad, kExchangeStore>), dim3(b.blocks), dim3(kThreads), 0, stream, b);
 }
 
 template <int L, int T>
@@ -446,6 +532,13 @@ static void launch_norm_rope_lanes(const NormRopeArgs &a, bool uniform, bool til
     else if (uniform) hipLaunchKernelGGL((norm_rope_kernel<L, T, true, false>), grid, block, 0, stream, a);
     else if (tile) hipLaunchKernelGGL((norm_rope_kernel<L, T, false, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((norm_rope_kernel<L, T, false, false>), grid, block, 0, stream, a);
+}
+
+void launch_norm_rope_band(const NormRopeArgs &a, int dtype, uint32_t blocks, hipStream_t stream) {
+    if (dtype == 2)
+        hipLaunchKernelGGL(norm_rope_band_kernel<2>, dim3(blocks), dim3(kBandWaves * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL(norm_rope_band_kernel<1>, dim3(blocks), dim3(kBandWaves * 64), 0, stream, a);
 }
 
 void launch_norm_rope(const NormRopeArgs &a, int lanes, int dtype, bool uniform, bool tile, uint32_t blocks,

@@ -641,7 +641,7 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
                             names[i]);
     if (c->route == ULY_ROUTE_CALLER) {
         // stream order on `caller` covers input readiness and target reuse
-        if ((st = launch(c, ULY_K_SCATTER, caller, [&] { launch_relayout(batch, false, caller); })) != ULY_OK)
+        if ((st = launch(c, ULY_K_SCATTER, caller, [&] { launch_relayout(batch, caller); })) != ULY_OK)
             return st;
         return mark_pending(c, caller);
     }
@@ -660,7 +660,7 @@ uly_status ulysses_scatter_qkv(uly_ctx *c, const uly_tensor *q, const uly_tensor
         if (cerr != hipSuccess) return poison(c, cerr, "hipMemcpy2DAsync");
         return mark_pending(c, c->comm);
     }
-    if ((st = launch(c, ULY_K_SCATTER, c->comm, [&] { launch_relayout(batch, false, c->comm); })) != ULY_OK)
+    if ((st = launch(c, ULY_K_SCATTER, c->comm, [&] { launch_relayout(batch, c->comm); })) != ULY_OK)
         return st;
     return mark_pending(c, c->comm);
 }
@@ -792,8 +792,26 @@ static uly_status fused_scatter(uly_ctx *c, const uly_tensor *q, const uly_tenso
     const bool tile = S % kRopeTokens == 0;
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
-    if ((st = launch(c, ULY_K_NORM_ROPE, caller,
-                     [&] { launch_norm_rope(a, lanes, dtype, uniform, tile, blocks, caller); })) != ULY_OK)
+    // Operands that are each one dense [P][B][S_l][H][D] tensor take the
+    // operand-major band form (the blocks in flight then read one tensor front
+    // to back); interleaved ones, such as Q/K/V views of a fused projection,
+    // the token-tile form, which reads each token's rows of all operands at once.
+    a.P = uint32_t(c->P);
+    uint32_t nops = 0;
+    bool dense = true;
+    for (int i = 0; i < 3; ++i) {
+        if (!Hrows[i]) continue;
+        a.task_op[nops++] = uint32_t(i);
+        const Operand &x = ops[i];
+        dense = dense && x.sh == x.D && x.ss == x.H * x.D && x.sb == x.S * x.ss && x.rank_stride == x.B * x.sb;
+    }
+    for (uint32_t i = nops; i < 3; ++i) a.task_op[i] = a.task_op[0];
+    const bool band = dense && lanes == 16 && S % kBandTokens == 0;
+    const uint32_t band_blocks = uint32_t(tokens / kBandTokens) * nops;
+    if ((st = launch(c, ULY_K_NORM_ROPE, caller, [&] {
+             if (band) launch_norm_rope_band(a, dtype, band_blocks, caller);
+             else launch_norm_rope(a, lanes, dtype, uniform, tile, blocks, caller);
+         })) != ULY_OK)
         return st;
     return mark_pending(c, caller);
 }
@@ -957,8 +975,7 @@ uly_status ulysses_gather_out(uly_ctx *c, const uly_tensor *o, const char *tag, 
     if (batch.n == 0) return ULY_OK;
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
-    const bool resident = 2 * int64_t(batch.p[0].total) * 16 <= kCacheResidentBytes;
-    return launch(c, ULY_K_GATHER, caller, [&] { launch_relayout(batch, resident, caller); });
+    return launch(c, ULY_K_GATHER, caller, [&] { launch_relayout(batch, caller); });
 }
 
 uly_status uly_exchange_chunks(uly_ctx *c, const void *x, void *y, int64_t chunk_bytes, hipStream_t stream) {
@@ -985,7 +1002,7 @@ uly_status uly_exchange_chunks(uly_ctx *c, const void *x, void *y, int64_t chunk
     if (batch.n == 0) return ULY_OK;
     DeviceGuard g(c->device);
     if (g.err != hipSuccess) return poison(c, g.err, "hipSetDevice");
-    return launch(c, ULY_K_SCATTER, stream, [&] { launch_relayout(batch, false, stream); });
+    return launch(c, ULY_K_SCATTER, stream, [&] { launch_relayout(batch, stream); });
 }
 
 // ---- sequence padding ------------------------------------------------------
