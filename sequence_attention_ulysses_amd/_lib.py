@@ -189,9 +189,25 @@ def int64_array(values):
     return (ctypes.c_int64 * len(values))(*[int(v) for v in values])
 
 
+_TAGS = {}
+
+
 def tags_array(tags):
-    return (ctypes.c_char_p * len(tags))(*[t.encode() if t is not None else None for t in tags])
+    """A C array of the tag strings (NULL for None).  The library only reads it, so one
+    array per distinct tags tuple is built and reused."""
+    tags = tuple(tags)
+    arr = _TAGS.get(tags)
+    if arr is None:
+        if len(_TAGS) > 1024:
+            _TAGS.clear()
+        arr = _TAGS[tags] = (ctypes.c_char_p * len(tags))(*[t.encode() if t is not None else None for t in tags])
+    return arr
+
+
+_PTRS3 = ctypes.c_void_p * 3
 
 
 def ptr_array(ptrs):
+    if len(ptrs) == 3:
+        return _PTRS3(ptrs[0] or None, ptrs[1] or None, ptrs[2] or None)
     return (ctypes.c_void_p * len(ptrs))(*[p if p else None for p in ptrs])

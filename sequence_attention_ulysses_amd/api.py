@@ -35,25 +35,31 @@ def _dtype_code(t) -> int:
         raise TypeError("supported: float16, bfloat16 and 1-byte types; got %s" % dtype) from None
 
 
-def _stream_handle(stream) -> ctypes.c_void_p:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+# The current stream's raw handle without building a torch Stream object
+# (torch.cuda.current_stream() costs ~3 us a call); torch's own compiled
+# kernels read it the same way.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_handle(stream, device=None) -> int:
+    """The HIP stream handle of `stream`, or of the current stream of `device`."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None and device is not None:
+        return _raw_stream(device)
+    return torch.cuda.current_stream().cuda_stream
+
+
+_I64x4 = ctypes.c_int64 * 4
 
 
 def describe(t: torch.Tensor) -> _lib.UlyTensor:
     """uly_tensor of a rank-major [P, B, S, H, D] tensor (no copy)."""
     if t.dim() != 5:
         raise ValueError("operand must be 5-D [P, B, S, H, D], got shape %s" % (tuple(t.shape),))
-    d = _lib.UlyTensor()
-    d.data = t.data_ptr() if t.numel() else 0
-    d.dtype = _dtype_code(t)
-    d.reserved = 0
-    d.rank_stride = t.stride(0)
-    for i in range(4):
-        d.shape[i] = t.shape[1 + i]
-        d.stride[i] = t.stride(1 + i)
-    return d
+    sh, st = t.shape, t.stride()
+    return _lib.UlyTensor(t.data_ptr() if t.numel() else 0, _dtype_code(t), 0, st[0],
+                          _I64x4(sh[1], sh[2], sh[3], sh[4]), _I64x4(st[1], st[2], st[3], st[4]))
 
 
 def rope_table_1d(rows: int, D: int, theta: float = 1e4, real_rows: int | None = None):
@@ -143,8 +149,11 @@ class UlyssesContext:
         for t in tensors:
             if t is None:
                 continue
-            if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.device.index != self.device:
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.get_device() != self.device:
                 raise ValueError("tensor must be on cuda:%s, got %s" % (self.device, getattr(t, "device", type(t))))
+
+    def _stream(self, stream) -> int:
+        return _stream_handle(stream, self.device)
 
     @staticmethod
     def _check_out(out: torch.Tensor, like_dtype, numel: int, what: str) -> None:
@@ -181,13 +190,43 @@ class UlyssesContext:
         self._targets[key] = view
         return view
 
-    def _dest(self, tag, mode, like: torch.Tensor, shape, out):
+    def _resolve(self, tag, mode, like: torch.Tensor, shape, out, pending: dict):
+        """A member's destination and the pointer the call passes for it.
+
+        An explicit `out` is passed as a pointer.  A key already registered is
+        passed as its tag alone (None), so the library resolves it from its cache.
+        A new key gets fresh storage, passed as a pointer, and is recorded in
+        `pending`: it is registered only once the library has accepted the call
+        (`_register`), so a rejected call leaves the cache as it was."""
         if out is not None:
             self._on_device(out)
             self._check_out(out, like.dtype, self.world_size * math.prod(shape), tag or "out")
-            return out, True
-        t = self.target(tag, mode, like.dtype, shape)
-        return t, (tag, mode, _dtype_code(like.dtype), tuple(int(x) for x in shape)) not in self._targets
+            return out, out.data_ptr()
+        if not tag:
+            raise ValueError("a cached target needs a tag (or pass an explicit destination)")
+        key = (tag, mode, _dtype_code(like.dtype), shape)
+        t = self._targets.get(key)
+        if t is not None:
+            return (t if t.dtype == like.dtype else t.view(like.dtype)), None
+        t = pending.get(key)
+        if t is None:
+            t = torch.empty((self.world_size,) + shape, dtype=like.dtype,
+                            device=torch.device("cuda", self.device))
+            pending[key] = t
+        return t, t.data_ptr()
+
+    def _register(self, pending: dict) -> None:
+        """Register the new targets of a call the library accepted."""
+        for key, t in pending.items():
+            tag, mode, code, shape = key
+            st = self._lib.uly_target_register(self._h(), tag.encode(), mode, code, _lib.int64_array(shape),
+                                               t.data_ptr(), t.numel() * t.element_size())
+            if st == _lib.E_CACHE_FULL:
+                warnings.warn("Ulysses target cache is full; '%s' used a one-shot buffer" % tag, RuntimeWarning,
+                              stacklevel=3)
+                continue
+            check(st, "uly_target_register")
+            self._targets[key] = t
 
     # -- the exchange -----------------------------------------------------------
     def scatter_qkv(self, q=None, k=None, v=None, tags=("q", "k", "v"), out=None, stream=None):
@@ -200,7 +239,7 @@ class UlyssesContext:
         P = self.world_size
         mem = (q, k, v)
         self._on_device(*mem)
-        descs, dests, ptrs = [], [], []
+        descs, dests, ptrs, pending = [], [], [], {}
         for i, x in enumerate(mem):
             if x is None:
                 descs.append(None); dests.append(None); ptrs.append(None)
@@ -209,13 +248,14 @@ class UlyssesContext:
                 # the library raises the precise error; shape here only sizes the target
                 descs.append(describe(x)); dests.append(None); ptrs.append(None)
                 continue
-            shape = (x.shape[1], x.shape[2] * P, x.shape[3] // P, x.shape[4])
-            d, explicit = self._dest(tags[i], _lib.MODE_SCATTER, x, shape, None if out is None else out[i])
-            descs.append(describe(x)); dests.append(d)
-            ptrs.append(d.data_ptr() if explicit else None)
+            sh = x.shape
+            d, ptr = self._resolve(tags[i], _lib.MODE_SCATTER, x, (sh[1], sh[2] * P, sh[3] // P, sh[4]),
+                                   None if out is None else out[i], pending)
+            descs.append(describe(x)); dests.append(d); ptrs.append(ptr)
         args = [ctypes.byref(dd) if dd is not None else None for dd in descs]
         check(self._lib.ulysses_scatter_qkv(self._h(), *args, _lib.tags_array(tags), _lib.ptr_array(ptrs),
-                                            _stream_handle(stream)), "ulysses_scatter_qkv")
+                                            self._stream(stream)), "ulysses_scatter_qkv")
+        self._register(pending)
         return dests
 
     def fused_qk_norm_rope_scatter(self, q, k, w_q, w_k, cos, sin, eps: float = 1e-6, v=None,
@@ -230,22 +270,7 @@ class UlyssesContext:
         mem = (q, k, v)
         _check_tables(cos, sin, None)
         self._on_device(q, k, v, w_q, w_k, cos, sin)
-        descs, dests, ptrs = [], [], []
-        for i, x in enumerate(mem):
-            if x is None:
-                descs.append(None); dests.append(None); ptrs.append(None)
-                continue
-            if x.dim() != 5 or x.shape[3] % P:
-                descs.append(describe(x)); dests.append(None); ptrs.append(None)
-                continue
-            shape = (x.shape[1], x.shape[2] * P, x.shape[3] // P, x.shape[4])
-            o_i = None if out is None or i >= len(out) else out[i]
-            d, explicit = self._dest(tags[i], _lib.MODE_SCATTER, x, shape, o_i)
-            descs.append(describe(x)); dests.append(d)
-            ptrs.append(d.data_ptr() if explicit else None)
-        args = [ctypes.byref(dd) if dd is not None else None for dd in descs]
-        wq = w_q.data_ptr() if (w_q is not None and q is not None) else None
-        wk = w_k.data_ptr() if (w_k is not None and k is not None) else None
+        # every Python-side check before any destination is resolved
         for w, x in ((w_q, q), (w_k, k)):
             if x is not None and w is not None and (w.dtype != x.dtype or not w.is_contiguous()
                                                     or w.numel() != x.shape[-1]):
@@ -254,10 +279,27 @@ class UlyssesContext:
             if x is not None and x.dim() == 5 and cos.shape[1] * 2 != x.shape[-1]:
                 raise ValueError("cos/sin tables must have D/2 columns")
         tags = tuple(tags) + (None,) * (3 - len(tags))
+        descs, dests, ptrs, pending = [], [], [], {}
+        for i, x in enumerate(mem):
+            if x is None:
+                descs.append(None); dests.append(None); ptrs.append(None)
+                continue
+            if x.dim() != 5 or x.shape[3] % P:
+                descs.append(describe(x)); dests.append(None); ptrs.append(None)
+                continue
+            sh = x.shape
+            o_i = None if out is None or i >= len(out) else out[i]
+            d, ptr = self._resolve(tags[i], _lib.MODE_SCATTER, x, (sh[1], sh[2] * P, sh[3] // P, sh[4]), o_i,
+                                   pending)
+            descs.append(describe(x)); dests.append(d); ptrs.append(ptr)
+        args = [ctypes.byref(dd) if dd is not None else None for dd in descs]
+        wq = w_q.data_ptr() if (w_q is not None and q is not None) else None
+        wk = w_k.data_ptr() if (w_k is not None and k is not None) else None
         check(self._lib.fused_qk_norm_rope_scatter(self._h(), *args, wq, wk, float(eps), cos.data_ptr(),
                                                    sin.data_ptr(), cos.shape[0], _lib.tags_array(tags),
-                                                   _lib.ptr_array(ptrs), _stream_handle(stream)),
+                                                   _lib.ptr_array(ptrs), self._stream(stream)),
               "fused_qk_norm_rope_scatter")
+        self._register(pending)
         return dests
 
     def fused_qkv_proj_norm_rope_scatter(self, x, w_qkv, Hq: int, Hkv: int, w_q, w_k, cos, sin, eps: float = 1e-6,
@@ -282,19 +324,19 @@ class UlyssesContext:
             if w.dtype != x.dtype or not w.is_contiguous() or w.numel() != D:
                 raise ValueError("norm weights must be contiguous [D] tensors in the activation dtype")
         B, S_l = x.shape[1], x.shape[2]
-        dests, ptrs = [], []
+        dests, ptrs, pending = [], [], {}
         for i, H in enumerate((Hq, Hkv, Hkv)):
             if H % P:
                 dests.append(None); ptrs.append(None)     # the library raises the precise error
                 continue
-            shape = (B, S_l * P, H // P, D)
             o_i = None if out is None else out[i]
-            d, explicit = self._dest(tags[i], _lib.MODE_SCATTER, x, shape, o_i)
-            dests.append(d); ptrs.append(d.data_ptr() if explicit else None)
+            d, ptr = self._resolve(tags[i], _lib.MODE_SCATTER, x, (B, S_l * P, H // P, D), o_i, pending)
+            dests.append(d); ptrs.append(ptr)
         check(self._lib.fused_qkv_proj_norm_rope_scatter(
             self._h(), x.data_ptr(), _dtype_code(x), B, S_l, x.shape[3], w_qkv.data_ptr(), Hq, Hkv, D,
             w_q.data_ptr(), w_k.data_ptr(), float(eps), cos.data_ptr(), sin.data_ptr(), cos.shape[0],
-            _lib.tags_array(tags), _lib.ptr_array(ptrs), _stream_handle(stream)), "fused_qkv_proj_norm_rope_scatter")
+            _lib.tags_array(tags), _lib.ptr_array(ptrs), self._stream(stream)), "fused_qkv_proj_norm_rope_scatter")
+        self._register(pending)
         return dests
 
     def fused_qkv_norm_rope_scatter_packed(self, q, k, v, w_q, w_k, cos, sin, eps: float = 1e-6, tag="qkv",
@@ -307,22 +349,20 @@ class UlyssesContext:
         for x in (q, k, v):
             if x.dim() != 5:
                 raise ValueError("operands must be 5-D [P, B, S_l, H, D]")
-        shape = (q.shape[1], q.shape[2] * P, q.shape[3] // P, 3 * q.shape[4])
-        if out is None and q.shape[3] % P == 0:
-            dest = self.target(tag, _lib.MODE_SCATTER, q.dtype, shape)
-            explicit = (tag, _lib.MODE_SCATTER, _dtype_code(q.dtype), shape) not in self._targets
-        else:
-            dest, explicit = out, out is not None
-            if out is not None:
-                self._check_out(out, q.dtype, P * math.prod(shape), tag or "out")
         for w in (w_q, w_k):
             if w.dtype != q.dtype or not w.is_contiguous() or w.numel() != q.shape[-1]:
                 raise ValueError("norm weights must be contiguous [D] tensors in the operand dtype")
+        shape = (q.shape[1], q.shape[2] * P, q.shape[3] // P, 3 * q.shape[4])
+        pending = {}
+        if out is None and q.shape[3] % P:
+            dest, ptr = None, None                        # the library raises the precise error
+        else:
+            dest, ptr = self._resolve(tag, _lib.MODE_SCATTER, q, shape, out, pending)
         check(self._lib.fused_qkv_norm_rope_scatter_packed(
             self._h(), ctypes.byref(describe(q)), ctypes.byref(describe(k)), ctypes.byref(describe(v)),
             w_q.data_ptr(), w_k.data_ptr(), float(eps), cos.data_ptr(), sin.data_ptr(), cos.shape[0],
-            tag.encode() if tag else None, dest.data_ptr() if explicit and dest is not None else None,
-            _stream_handle(stream)), "fused_qkv_norm_rope_scatter_packed")
+            tag.encode() if tag else None, ptr, self._stream(stream)), "fused_qkv_norm_rope_scatter_packed")
+        self._register(pending)
         return dest
 
     def exchange_chunks(self, x, out=None, stream=None):
@@ -339,12 +379,12 @@ class UlyssesContext:
         chunk = x.numel() * x.element_size() // (P * P)
         check(self._lib.uly_exchange_chunks(self._h(), x.data_ptr() if x.numel() else None,
                                             out.data_ptr() if out.numel() else None, chunk,
-                                            _stream_handle(stream)), "uly_exchange_chunks")
+                                            self._stream(stream)), "uly_exchange_chunks")
         return out
 
     def wait(self, stream=None) -> None:
         """Grouped handshake: ``stream`` (default: current) waits for all scatters since the last wait."""
-        check(self._lib.uly_wait(self._h(), _stream_handle(stream)), "uly_wait")
+        check(self._lib.uly_wait(self._h(), self._stream(stream)), "uly_wait")
 
     def gather_out(self, o, tag: str = "out", out=None, stream=None) -> torch.Tensor:
         """Head-sharded [P, B, S, Hl, D] -> sequence-sharded [P, B, S/P, P*Hl, D] on the caller's stream."""
@@ -352,17 +392,16 @@ class UlyssesContext:
         self._on_device(o, out)
         if o.dim() != 5:
             raise ValueError("operand must be 5-D [P, B, S, Hl, D]")
-        if out is not None:
-            self._check_out(out, o.dtype, o.numel(), "gather_out")
-        shape = (o.shape[1], o.shape[2] // P, o.shape[3] * P, o.shape[4])
-        if out is None and o.shape[2] % P == 0:
-            dest = self.target(tag, _lib.MODE_GATHER, o.dtype, shape)
-            explicit = (tag, _lib.MODE_GATHER, _dtype_code(o.dtype), tuple(int(x) for x in shape)) not in self._targets
+        sh = o.shape
+        shape = (sh[1], sh[2] // P, sh[3] * P, sh[4])
+        pending = {}
+        if out is None and sh[2] % P:
+            dest, ptr = None, None                        # the library raises the precise error
         else:
-            dest, explicit = out, out is not None
+            dest, ptr = self._resolve(tag, _lib.MODE_GATHER, o, shape, out, pending)
         check(self._lib.ulysses_gather_out(self._h(), ctypes.byref(describe(o)), tag.encode() if tag else None,
-                                           dest.data_ptr() if explicit and dest is not None else None,
-                                           _stream_handle(stream)), "ulysses_gather_out")
+                                           ptr, self._stream(stream)), "ulysses_gather_out")
+        self._register(pending)
         return dest
 
     # -- sequence padding ---------------------------------------------------------
@@ -377,7 +416,7 @@ class UlyssesContext:
             out = torch.empty((self.world_size, B, S_l) + row, dtype=full.dtype, device=full.device)
         self._check_out(out, full.dtype, self.world_size * B * S_l * math.prod(row), "seq_pad_shard")
         check(self._lib.uly_seq_pad_shard(self._h(), full.data_ptr(), _dtype_code(full), B, S,
-                                          math.prod(row), S_l, out.data_ptr(), _stream_handle(stream)),
+                                          math.prod(row), S_l, out.data_ptr(), self._stream(stream)),
               "uly_seq_pad_shard")
         return out
 
@@ -392,7 +431,7 @@ class UlyssesContext:
             out = torch.empty((B, S) + row, dtype=x.dtype, device=x.device)
         self._check_out(out, x.dtype, B * S * math.prod(row), "seq_unshard_trim")
         check(self._lib.uly_seq_unshard_trim(self._h(), x.data_ptr(), _dtype_code(x), B, S, math.prod(row),
-                                             S_l, out.data_ptr(), _stream_handle(stream)), "uly_seq_unshard_trim")
+                                             S_l, out.data_ptr(), self._stream(stream)), "uly_seq_unshard_trim")
         return out
 
     # -- spatial height shards ----------------------------------------------------
@@ -409,7 +448,7 @@ class UlyssesContext:
         self._check_out(out, full.dtype, self.world_size * math.prod(lead) * (hmax + 2 * halo) * W,
                         "spatial_split_halo")
         check(self._lib.uly_spatial_split_halo(self._h(), full.data_ptr(), _dtype_code(full), math.prod(lead),
-                                               Hh, W, halo, out.data_ptr(), _stream_handle(stream)),
+                                               Hh, W, halo, out.data_ptr(), self._stream(stream)),
               "uly_spatial_split_halo")
         return out
 
@@ -428,7 +467,7 @@ class UlyssesContext:
                         "spatial_gather_stacked")
         check(self._lib.uly_spatial_gather_stacked(self._h(), shards.data_ptr(), _dtype_code(shards),
                                                    math.prod(lead), Hh, W, halo, out.data_ptr(),
-                                                   _stream_handle(stream)), "uly_spatial_gather_stacked")
+                                                   self._stream(stream)), "uly_spatial_gather_stacked")
         return out
 
     def spatial_trim_concat(self, stacked: torch.Tensor, Hh: int, out=None, stream=None) -> torch.Tensor:
@@ -443,7 +482,7 @@ class UlyssesContext:
             out = torch.empty(lead + (Hh, W), dtype=stacked.dtype, device=stacked.device)
         self._check_out(out, stacked.dtype, math.prod(lead) * Hh * W, "spatial_trim_concat")
         check(self._lib.uly_spatial_trim_concat(self._h(), stacked.data_ptr(), _dtype_code(stacked),
-                                                math.prod(lead), Hh, W, out.data_ptr(), _stream_handle(stream)),
+                                                math.prod(lead), Hh, W, out.data_ptr(), self._stream(stream)),
               "uly_spatial_trim_concat")
         return out
 

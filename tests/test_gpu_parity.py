@@ -517,6 +517,31 @@ def test_consumer_on_other_stream_sees_results(dev, orc):
                    "bf16", "q")
 
 
+def test_rejected_call_registers_nothing(dev):
+    """A call the library rejects leaves the target cache as it was: new keys are
+    registered only after the library accepted the call."""
+    P, B, S_l, H, D = 2, 1, 16, 4, 128
+    q = synth.normal((P, B, S_l, H, D), "bf16", 70, dev)
+    w = synth.norm_weight(D, "bf16", 71, dev)
+    cos, sin = (t.to(dev) for t in rope_table_1d(P * S_l, D))
+    o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 72, dev)
+    with UlyssesContext(P, device=0) as ctx:
+        with pytest.raises(ValueError, match="eps"):
+            ctx.fused_qk_norm_rope_scatter(q, None, w, None, cos, sin, eps=0.0, tags=("qa", None, None))
+        with pytest.raises(ValueError, match="table"):
+            ctx.fused_qk_norm_rope_scatter(q, None, w, None, cos[:3], sin[:3], tags=("qb", None, None))
+        with pytest.raises(ValueError):
+            ctx.gather_out(o[:, :, :P * S_l - 1], tag="oa")          # sequence not divisible by P
+        assert ctx.target_count() == 0 and ctx.stats()["registrations"] == 0
+        (y, _, _) = ctx.fused_qk_norm_rope_scatter(q, None, w, None, cos, sin, tags=("qc", None, None))
+        z = ctx.gather_out(o, tag="oc")
+        (y2, _, _) = ctx.fused_qk_norm_rope_scatter(q, None, w, None, cos, sin, tags=("qc", None, None))
+        torch.cuda.synchronize()
+        assert ctx.target_count() == 2 and ctx.stats()["registrations"] == 2
+        assert y2.data_ptr() == y.data_ptr() and torch.equal(y2.view(torch.int16), y.view(torch.int16))
+        assert ctx.gather_out(o, tag="oc").data_ptr() == z.data_ptr()
+
+
 def test_target_reuse_waits_for_consumer(dev, orc):
     """Step n+1's scatter into a cached target is ordered after step n's consumer
     on the caller stream, even when that consumer is slow."""
