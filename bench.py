@@ -23,7 +23,8 @@ records, "Export-protocol validation"):
     every byte a step writes is charged to the steps (a write-back still in
     flight when a step's last kernel ends delays the next step);
   * the headline is the median of exactly --steps such steps (p10 and p90
-    beside it);
+    beside it), after --warmup untimed steps and a 0.2 s untimed pre-heat
+    that lets the clocks settle under the load;
   * an A/A repeat of the same measurement that drifts by more than 2 %
     marks the record invalid, with the reason;
   * the dominant kernel is timed on at least 10 launches by the library's
@@ -52,6 +53,7 @@ METRIC = "Ulysses QKV scatter+gather GB/s and % HBM peak, P=4 bf16, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 AA_MAX_DRIFT = 0.02          # an A/A repeat further off than this voids the record
 MIN_TIMED_LAUNCHES = 10      # launches of the dominant kernel timed whatever --steps is
+PREHEAT_S = 0.2              # untimed steps run before the warmup, in seconds of wall time
 KERNEL_SOURCES = [os.path.join(ROOT, "sequence_attention_ulysses_amd", "csrc", f)
                   for f in ("uly_kernels.hip", "uly_internal.h", "fastdiv.h")]
 
@@ -664,6 +666,18 @@ def main():
     if args.graph:
         args.no_profile = args.no_two_stream = True
         steps_per_operator = None
+    # Pre-heat: untimed steps for PREHEAT_S of wall time before the warmup, so
+    # that the clocks have settled under this load (the MFMA-bound projection
+    # runs its first ~15 ms of back-to-back steps up to 9 % slower).
+    torch.cuda.synchronize()
+    t0, n_pre = time.perf_counter(), 0
+    while time.perf_counter() - t0 < PREHEAT_S and n_pre < 5000:
+        steps[n_pre % R]()
+        n_pre += 1
+        if n_pre % R == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    preheat = {"steps": n_pre, "s": round(time.perf_counter() - t0, 3)}
     for i in range(max(args.warmup, R)):
         steps[i % R]()
         if not args.no_two_stream:
@@ -809,6 +823,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "valid": not invalid,
+        "preheat": preheat,
         "timing": "median of %d steps run back to back over %d rotating input/output sets (no data a step "
                   "reads is cached from the step before), HIP events between the steps" % (args.steps, R),
         "step_spread": headline,
