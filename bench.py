@@ -23,8 +23,9 @@ records, "Export-protocol validation"):
     every byte a step writes is charged to the steps (a write-back still in
     flight when a step's last kernel ends delays the next step);
   * the headline is the median of exactly --steps such steps (p10 and p90
-    beside it), after --warmup untimed steps and a 0.2 s untimed pre-heat
-    that lets the clocks settle under the load;
+    beside it), after --warmup untimed steps and an untimed pre-heat (at
+    least 0.2 s, until two passes of steps agree within 1 %) that lets the
+    clocks settle under the load;
   * an A/A repeat of the same measurement that drifts by more than 2 %
     marks the record invalid, with the reason;
   * the dominant kernel is timed on at least 10 launches by the library's
@@ -53,7 +54,8 @@ METRIC = "Ulysses QKV scatter+gather GB/s and % HBM peak, P=4 bf16, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 AA_MAX_DRIFT = 0.02          # an A/A repeat further off than this voids the record
 MIN_TIMED_LAUNCHES = 10      # launches of the dominant kernel timed whatever --steps is
-PREHEAT_S = 0.2              # untimed steps run before the warmup, in seconds of wall time
+PREHEAT_S = 0.2              # untimed steps run before the warmup: at least this long (s) ...
+PREHEAT_MAX_S = 3.0          # ... and at most this long, until two passes agree within 1 %
 KERNEL_SOURCES = [os.path.join(ROOT, "sequence_attention_ulysses_amd", "csrc", f)
                   for f in ("uly_kernels.hip", "uly_internal.h", "fastdiv.h")]
 
@@ -666,24 +668,26 @@ def main():
     if args.graph:
         args.no_profile = args.no_two_stream = True
         steps_per_operator = None
-    # Pre-heat: untimed steps for PREHEAT_S of wall time before the warmup, so
-    # that the clocks have settled under this load (the MFMA-bound projection
-    # runs its first ~15 ms of back-to-back steps up to 9 % slower).
-    torch.cuda.synchronize()
-    t0, n_pre = time.perf_counter(), 0
-    while time.perf_counter() - t0 < PREHEAT_S and n_pre < 5000:
-        steps[n_pre % R]()
-        n_pre += 1
-        if n_pre % R == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    preheat = {"steps": n_pre, "s": round(time.perf_counter() - t0, 3)}
+    # Pre-heat: untimed passes of back-to-back steps before the warmup until the
+    # clocks have settled under this load: at least PREHEAT_S of wall time and
+    # two consecutive passes within 1 % of each other, at most PREHEAT_MAX_S
+    # (the MFMA-bound projection runs its first ~15 ms of back-to-back steps
+    # up to 9 % slower than the rest).
+    t0, n_pre, prev, settled = time.perf_counter(), 0, None, False
+    per_pass = max(R, 10)
+    while time.perf_counter() - t0 < PREHEAT_MAX_S:
+        _, _, tot = back_to_back(torch, steps, per_pass)
+        n_pre += per_pass
+        settled = prev is not None and abs(tot / prev - 1.0) < 0.01
+        prev = tot
+        if settled and time.perf_counter() - t0 >= PREHEAT_S:
+            break
+    preheat = {"steps": n_pre, "s": round(time.perf_counter() - t0, 3), "settled": settled}
+    # (the forms timed beside the headline get their own warmup right before
+    # their measurement: interleaving another path's kernels here, a library
+    # GEMM say, leaves the next ~20 fused projection steps up to 20 % slower)
     for i in range(max(args.warmup, R)):
         steps[i % R]()
-        if not args.no_two_stream:
-            steps_two_stream[i % R]()
-        if steps_per_operator is not None:
-            steps_per_operator[i % R]()
     torch.cuda.synchronize()
     if args.graph:
         # the library's calls are capturable: a step with explicit destinations
@@ -781,11 +785,14 @@ def main():
     # the two-stream form of the same step, timed like the headline
     two_stream = None
     if not args.no_two_stream:
+        for i in range(max(args.warmup, R)):
+            steps_two_stream[i % R]()
         t2, _, _ = back_to_back(torch, steps_two_stream, args.steps)
         two_stream = spread(t2, work, unit_div, unit)
 
     per_operator = None
     if steps_per_operator is not None:
+        back_to_back(torch, steps_per_operator, max(args.steps, 2 * R))      # its warmup (~20 steps settle)
         t3, _, _ = back_to_back(torch, steps_per_operator, args.steps)
         per_operator = dict(spread(t3, work, unit_div, unit),
                             path="torch linear (hipBLASLt) writing qkv, then fused_qk_norm_rope_scatter, wait, gather",
