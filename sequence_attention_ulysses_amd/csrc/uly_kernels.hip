@@ -325,6 +325,18 @@ __global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_ker
         for (int u = 0; u < SU; ++u) wraw[u] = load16_cached(sl[u].w);
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
+            if (UNI && !sl[u].rope) {
+                // a V slot (wave-uniform here): the rows are stored as loaded,
+                // without the discarded norm and rotation (0.5 % of the step)
+#pragma unroll
+                for (int t = 0; t < TU; ++t) {
+                    const uint32_t g = tr[t] * a.S_l + ts[t];
+                    if (sl[u].live && live[t])
+                        store16<kRopeNtStore>(sl[u].dst + (int64_t(tb[t]) * sl[u].d_b + int64_t(g) * sl[u].d_g),
+                                              raw[u][t]);
+                }
+                continue;
+            }
             float w[8];
             unpack8<DT>(wraw[u], w);
 #pragma unroll
@@ -414,6 +426,13 @@ __global__ __launch_bounds__(kBandWaves * 64) void norm_rope_band_kernel(NormRop
                 hl.divmod(k, tt[u], jj[u]);
                 raw[u] = load16<kRopeNtLoad>(src + int64_t(tt[u]) * s_s + int64_t(jj[u]) * s_h);
             }
+            if (!rope) {                                     // a V block (block-uniform): rows as loaded
+#pragma unroll
+                for (int u = 0; u < MAXT; ++u)
+                    if (k0 + u * GPW + gi < rows)
+                        store16<kRopeNtStore>(dst + int64_t(tt[u]) * d_g + int64_t(jj[u]) * d_j, raw[u]);
+                continue;
+            }
             float w[8];
             unpack8<DT>(wraw, w);
 #pragma unroll
@@ -440,8 +459,9 @@ __global__ __launch_bounds__(kBandWaves * 64) void norm_rope_band_kernel(NormRop
                     const float n1 = x[2 * p + 1] * inv * w[2 * p + 1];
                     out[p] = pack2<DT>(n0 * c[p] - n1 * sv[p], n0 * sv[p] + n1 * c[p]);
                 }
-                const uint4 res = rope ? make_uint4(out[0], out[1], out[2], out[3]) : raw[u];
-                if (k < rows) store16<kRopeNtStore>(dst + int64_t(tt[u]) * d_g + int64_t(jj[u]) * d_j, res);
+                if (k < rows)
+                    store16<kRopeNtStore>(dst + int64_t(tt[u]) * d_g + int64_t(jj[u]) * d_j,
+                                          make_uint4(out[0], out[1], out[2], out[3]));
             }
         }
     }
