@@ -192,6 +192,29 @@ __device__ __forceinline__ T sel3(uint32_t i, T a, T b, T c) {
     return i == 0 ? a : (i == 1 ? b : c);
 }
 
+// One lane's eight values of a row: RMSNorm with its weights, then the
+// rotation of the lane's four interleaved pairs, each result rounded once to
+// 16 bits.  The rotation's products are combined in explicit fused
+// multiply-adds, y0 = fma(n0, c, -(n1 s)) and y1 = fma(n0, s, n1 c), so every
+// kernel that calls this rounds the same way whichever products the compiler
+// would otherwise have contracted.  The row's sum of squares comes in `ss`.
+template <int DT>
+__device__ __forceinline__ uint4 norm_rope8(const float (&x)[8], float ss, const float (&w)[8], float4 c4, float4 s4,
+                                            float inv_D, float eps) {
+    // eps > 0 keeps the argument normal: the bare reciprocal square root suffices
+    const float inv = __builtin_amdgcn_rsqf(fmaf(ss, inv_D, eps));
+    const float c[4] = {c4.x, c4.y, c4.z, c4.w};
+    const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float n0 = (x[2 * p] * inv) * w[2 * p];
+        const float n1 = (x[2 * p + 1] * inv) * w[2 * p + 1];
+        out[p] = pack2<DT>(fmaf(n0, c[p], -(n1 * sv[p])), fmaf(n0, sv[p], n1 * c[p]));
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 // Work mapping.  A block owns a tile of kRopeTokens consecutive tokens
 // (source order r, b, s).  Its GROUPS lane groups split the R = H0+H1+H2
 // rows of a token: group gi owns the row slots hh = gi, gi + GROUPS, ...,
@@ -350,20 +373,8 @@ __global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_ker
 #pragma unroll
                 for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
                 ss = row_sum<LANES>(ss);
-                // eps > 0 keeps the argument normal: the bare reciprocal square root suffices
-                const float inv = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_D, a.eps));
-                const float c[4] = {cs[t].x, cs[t].y, cs[t].z, cs[t].w};
-                const float sv[4] = {sn[t].x, sn[t].y, sn[t].z, sn[t].w};
-                uint32_t out[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float n0 = x[2 * p] * inv * w[2 * p];
-                    const float n1 = x[2 * p + 1] * inv * w[2 * p + 1];
-                    const float y0 = n0 * c[p] - n1 * sv[p];
-                    const float y1 = n0 * sv[p] + n1 * c[p];
-                    out[p] = pack2<DT>(y0, y1);
-                }
-                const uint4 res = sl[u].rope ? make_uint4(out[0], out[1], out[2], out[3]) : raw[u][t];
+                const uint4 rot = norm_rope8<DT>(x, ss, w, cs[t], sn[t], a.inv_D, a.eps);
+                const uint4 res = sl[u].rope ? rot : raw[u][t];
                 const uint32_t g = tr[t] * a.S_l + ts[t];
                 if (sl[u].live && live[t])
                     store16<kRopeNtStore>(sl[u].dst + (int64_t(tb[t]) * sl[u].d_b + int64_t(g) * sl[u].d_g), res);
@@ -447,24 +458,13 @@ __global__ __launch_bounds__(kBandWaves * 64) void norm_rope_band_kernel(NormRop
 #pragma unroll
                 for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
                 ss = row_sum<LANES>(ss);
-                // eps > 0 keeps the argument normal: the bare reciprocal square root suffices
-                const float inv = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_D, a.eps));
                 float4 c4 = cs[0], s4 = sn[0];
 #pragma unroll
                 for (int t = 1; t < TU; ++t)
                     if (tt[u] == uint32_t(t)) { c4 = cs[t]; s4 = sn[t]; }
-                const float c[4] = {c4.x, c4.y, c4.z, c4.w};
-                const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-                uint32_t out[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float n0 = x[2 * p] * inv * w[2 * p];
-                    const float n1 = x[2 * p + 1] * inv * w[2 * p + 1];
-                    out[p] = pack2<DT>(n0 * c[p] - n1 * sv[p], n0 * sv[p] + n1 * c[p]);
-                }
+                const uint4 rot = norm_rope8<DT>(x, ss, w, c4, s4, a.inv_D, a.eps);
                 if (k < rows)
-                    store16<kRopeNtStore>(dst + int64_t(tt[u]) * d_g + int64_t(jj[u]) * d_j,
-                                          make_uint4(out[0], out[1], out[2], out[3]));
+                    store16<kRopeNtStore>(dst + int64_t(tt[u]) * d_g + int64_t(jj[u]) * d_j, rot);
             }
         }
     }

@@ -317,7 +317,8 @@ __device__ __forceinline__ void proj_epilogue(const ProjArgs &a, accv_t (&acc)[k
         for (int nb = 0; nb < 4; ++nb) {
             uint32_t pk[8];   // pk[2*grp + p]: the pair (d0 + 2p, d0 + 2p + 1) of register group grp
             if constexpr (QK) {
-                // pairs j0 = 16nb + 4grp + 2half and j0 + 1: chunk j0 / 2 of the row
+                // pairs j0 = 16nb + 4grp + 2half and j0 + 1: chunk j0 / 2 of the row;
+                // the rotation in explicit fused multiply-adds, as in the exchange kernels
                 float4 cs[4];
 #pragma unroll
                 for (int grp = 0; grp < 4; ++grp) cs[grp] = trow[nb * 8 + grp * 2 + half];
@@ -329,7 +330,7 @@ __device__ __forceinline__ void proj_epilogue(const ProjArgs &a, accv_t (&acc)[k
                         const int i0 = grp * 4 + p * 2;
                         const float n0 = acc[nb][tb][i0] * inv * wf[nb][grp][2 * p];
                         const float n1 = acc[nb][tb][i0 + 1] * inv * wf[nb][grp][2 * p + 1];
-                        pk[grp * 2 + p] = pack2<DT>(n0 * cv[p] - n1 * sv[p], n0 * sv[p] + n1 * cv[p]);
+                        pk[grp * 2 + p] = pack2<DT>(fmaf(n0, cv[p], -(n1 * sv[p])), fmaf(n0, sv[p], n1 * cv[p]));
                     }
                 }
             } else {
@@ -432,14 +433,14 @@ __device__ __forceinline__ void proj_epilogue16(const ProjArgs &a, accv_t (&acc)
                 const int nb = 2 * nbp + h;
                 uint32_t pk[2];
                 if constexpr (QK) {
-                    // pairs j0 = 8nb + 2q and j0 + 1: chunk j0 / 2 of the row
+                    // pairs j0 = 8nb + 2q and j0 + 1: chunk j0 / 2 of the row (explicit fmas)
                     const float4 cs = trow[4 * nb + q];
 #pragma unroll
                     for (int p = 0; p < 2; ++p) {
                         const float cv = p ? cs.z : cs.x, sv = p ? cs.w : cs.y;
                         const float n0 = acc[nb][tb][2 * p] * inv * wf[nb][2 * p];
                         const float n1 = acc[nb][tb][2 * p + 1] * inv * wf[nb][2 * p + 1];
-                        pk[p] = pack2<DT>(n0 * cv - n1 * sv, n0 * sv + n1 * cv);
+                        pk[p] = pack2<DT>(fmaf(n0, cv, -(n1 * sv)), fmaf(n0, sv, n1 * cv));
                     }
                 } else {
 #pragma unroll

@@ -195,6 +195,30 @@ def test_fused_norm_rope_small(dev, orc, P, B, S_l, Hq, Hkv, D, dtype, fused):
         assert torch.equal(yk2.view(torch.int16), yk.view(torch.int16))
 
 
+@pytest.mark.parametrize("P,B,S_l,Hq,Hkv", [(4, 1, 64, 24, 24), (8, 2, 16, 32, 8), (2, 1, 10, 40, 40), (1, 1, 6, 4, 2)])
+def test_dense_and_interleaved_operands_agree(dev, orc, P, B, S_l, Hq, Hkv):
+    """Dense Q/K/V tensors take the operand-major band kernel, the same values as views
+    of one interleaved tensor the token-tile kernel: the per-row arithmetic is the same,
+    so the results must agree bit for bit (and with the oracle)."""
+    D = 128
+    q, k, v = contiguous_qkv(P, B, S_l, Hq, D, "bf16", 77, dev, Hkv)
+    # the same values, interleaved: [P, B, S_l, Hq + 2 Hkv, D] with q, k, v head ranges
+    inter = torch.cat([q, k, v], dim=3).contiguous()
+    qi, ki, vi = inter[:, :, :, :Hq], inter[:, :, :, Hq:Hq + Hkv], inter[:, :, :, Hq + Hkv:]
+    w_q, w_k = synth.norm_weight(D, "bf16", 78, dev), synth.norm_weight(D, "bf16", 79, dev)
+    cos, sin = (t.to(dev) for t in rope_table_1d(P * S_l, D))
+    with UlyssesContext(P, device=0) as ctx:
+        yd = ctx.fused_qk_norm_rope_scatter(q, k, w_q, w_k, cos, sin, v=v, tags=("dq", "dk", "dv"))
+        yi = ctx.fused_qk_norm_rope_scatter(qi, ki, w_q, w_k, cos, sin, v=vi, tags=("iq", "ik", "iv"))
+        ctx.wait()
+        torch.cuda.synchronize()
+        for a, b_, name in zip(yd, yi, "qkv"):
+            assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), name
+        ocos, osin = orc.rope_table_1d(P * S_l, D)
+        assert_close16(yd[0], orc.fused_norm_rope_scatter(to_bits(q), "bf16", to_bits(w_q), 1e-6, ocos, osin), "bf16", "q")
+        np.testing.assert_array_equal(to_bits(yd[2]), orc.scatter(to_bits(v)))
+
+
 def test_fused_single_operand_and_determinism(dev, orc):
     P, B, S_l, H, D = 4, 1, 96, 8, 128
     k = synth.normal((P, B, S_l, H, D), "bf16", 8, dev)
