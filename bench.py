@@ -56,8 +56,9 @@ AA_MAX_DRIFT = 0.02          # an A/A repeat further off than this voids the rec
 MIN_TIMED_LAUNCHES = 10      # launches of the dominant kernel timed whatever --steps is
 PREHEAT_S = 0.2              # untimed steps run before the warmup: at least this long (s) ...
 PREHEAT_MAX_S = 3.0          # ... and at most this long, until two passes agree within 1 %
+# the kernels and the runtime that decides which kernel moves which operand
 KERNEL_SOURCES = [os.path.join(ROOT, "sequence_attention_ulysses_amd", "csrc", f)
-                  for f in ("uly_kernels.hip", "uly_internal.h", "fastdiv.h")]
+                  for f in ("uly_kernels.hip", "uly_internal.h", "fastdiv.h", "uly_runtime.cpp")]
 
 
 def kernel_source_hash() -> str:
@@ -243,7 +244,8 @@ def setup_wan_long(torch, dev, synth, rope_table_1d, UlyssesContext, sets=3):
 
         steps.append(step)
     return {"workload": w, "ctx": ctx, "steps": steps, "bytes_per_step": 3 * 2 * real + 2 * real,
-            "dominant": ("norm_rope", 6 * real, "norm_rope_kernel<16,bf16> (3-D RoPE, padded sequence)"),
+            "dominant": ("norm_rope", 4 * real,
+                         "norm_rope_band_kernel<bf16> (Q/K, 3-D RoPE, padded sequence; V by the relayout kernel)"),
             "dtype": "bf16", "data": "synthetic N(0,1) activations, N(1,0.1) norm weights, 3-D RoPE 44/42/42",
             "config": {"workload": w.name, "P": P, "B": B, "S": S, "S_padded": P * S_l, "H": H, "D": D,
                        "bytes_per_step": 3 * 2 * real + 2 * real, "bytes_count": "real tokens only"}}

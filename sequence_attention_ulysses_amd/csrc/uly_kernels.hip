@@ -393,7 +393,10 @@ __global__ __launch_bounds__(kRopeThreads) ULY_ROPE_OCCUPANCY void norm_rope_ker
 // contiguous run of the destination (Hl * tokens * D elements).  The wave
 // walks the run four rows at a time (one per 16-lane group), so every store
 // instruction writes 1 KiB of consecutive destination bytes.  D = 128
-// (16 lanes per row).
+// (16 lanes per row).  V blocks store their rows as loaded; the runtime
+// hands this kernel V only for the packed receive layout, and moves a V
+// with a target of its own by the relayout kernel, which copies dense
+// operands at the plain copy rate.
 template <int DT>
 __global__ __launch_bounds__(kBandWaves * 64) void norm_rope_band_kernel(NormRopeArgs a) {
     constexpr int LANES = 16, GPW = 64 / LANES, TU = kBandTokens, MAXT = kBandInflight;

@@ -197,9 +197,10 @@ def test_fused_norm_rope_small(dev, orc, P, B, S_l, Hq, Hkv, D, dtype, fused):
 
 @pytest.mark.parametrize("P,B,S_l,Hq,Hkv", [(4, 1, 64, 24, 24), (8, 2, 16, 32, 8), (2, 1, 10, 40, 40), (1, 1, 6, 4, 2)])
 def test_dense_and_interleaved_operands_agree(dev, orc, P, B, S_l, Hq, Hkv):
-    """Dense Q/K/V tensors take the operand-major band kernel, the same values as views
-    of one interleaved tensor the token-tile kernel: the per-row arithmetic is the same,
-    so the results must agree bit for bit (and with the oracle)."""
+    """Dense Q/K/V tensors take the operand-major band kernel for Q/K and the relayout
+    kernel for V (two launches), the same values as views of one interleaved tensor the
+    token-tile kernel with V in the same launch: the per-row arithmetic is the same, so
+    the results must agree bit for bit (and with the oracle)."""
     D = 128
     q, k, v = contiguous_qkv(P, B, S_l, Hq, D, "bf16", 77, dev, Hkv)
     # the same values, interleaved: [P, B, S_l, Hq + 2 Hkv, D] with q, k, v head ranges
@@ -208,8 +209,11 @@ def test_dense_and_interleaved_operands_agree(dev, orc, P, B, S_l, Hq, Hkv):
     w_q, w_k = synth.norm_weight(D, "bf16", 78, dev), synth.norm_weight(D, "bf16", 79, dev)
     cos, sin = (t.to(dev) for t in rope_table_1d(P * S_l, D))
     with UlyssesContext(P, device=0) as ctx:
+        n0 = ctx.stats()["launches"]
         yd = ctx.fused_qk_norm_rope_scatter(q, k, w_q, w_k, cos, sin, v=v, tags=("dq", "dk", "dv"))
+        n1 = ctx.stats()["launches"]
         yi = ctx.fused_qk_norm_rope_scatter(qi, ki, w_q, w_k, cos, sin, v=vi, tags=("iq", "ik", "iv"))
+        assert (n1 - n0, ctx.stats()["launches"] - n1) == (2, 1)
         ctx.wait()
         torch.cuda.synchronize()
         for a, b_, name in zip(yd, yi, "qkv"):
@@ -236,15 +240,21 @@ def test_fused_single_operand_and_determinism(dev, orc):
                        "bf16", "k")
 
 
-def test_fused_v_only_is_a_plain_scatter(dev, orc):
-    """A fused call with V alone (no row is normalised) still reads a table row and a
-    weight row per slot without a branch; its output is the bit-exact scatter."""
+@pytest.mark.parametrize("layout", ["dense", "strided"])
+def test_fused_v_only_is_a_plain_scatter(dev, orc, layout):
+    """A fused call with V alone (no row is normalised) gives the bit-exact scatter.  A
+    dense V goes through the relayout kernel alone; a strided one (a view into a wider
+    tensor) through the token-tile kernel, which still reads a table row and a weight row
+    per slot without a branch."""
     P, B, S_l, H, D = 4, 2, 40, 8, 128
-    v = synth.normal((P, B, S_l, H, D), "bf16", 12, dev)
+    wide = synth.normal((P, B, S_l, 2 * H, D), "bf16", 12, dev)
+    v = wide[:, :, :, :H].contiguous() if layout == "dense" else wide[:, :, :, H:]
     cos, sin = rope_table_1d(P * S_l, D)
     with UlyssesContext(P, device=0) as ctx:
+        before = ctx.stats()["launches"]
         _, _, yv = ctx.fused_qk_norm_rope_scatter(None, None, None, None, cos.to(dev), sin.to(dev), v=v,
                                                   tags=(None, None, "v_only"))
+        assert ctx.stats()["launches"] == before + 1
         ctx.wait()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(to_bits(yv), orc.scatter(to_bits(v)))
