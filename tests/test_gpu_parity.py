@@ -744,7 +744,10 @@ def _random_case(rng):
 def test_random_shapes_all_paths(dev, orc, seed):
     """Random world sizes, head counts, head dims, tails, dtypes and source row
     padding through the plain scatter, the fused norm + RoPE scatter (with V) and
-    the gather, each against the oracle."""
+    the gather, each against the oracle.  The fused call runs twice: on views of the
+    one interleaved tensor (the token-tile kernel) and on dense copies (for D = 128
+    and even S_l the band kernel with V by the relayout kernel); both give the same
+    bits."""
     rng = np.random.default_rng(1000 + seed)
     P, B, S_l, Hq, Hk, D, dtype, pad = _random_case(rng)
     print("case P=%d B=%d S_l=%d Hq=%d Hk=%d D=%d %s pad=%d" % (P, B, S_l, Hq, Hk, D, dtype, pad), flush=True)
@@ -770,6 +773,13 @@ def test_random_shapes_all_paths(dev, orc, seed):
         for x, w, y, name in ((q, w_q, yq, "q"), (k, w_k, yk, "k")):
             ref = orc.fused_norm_rope_scatter(to_bits(x.contiguous()), dtype, to_bits(w), 1e-6, ocos, osin)
             assert_close16(y, ref, dtype, name)
+        qd, kd, vd = (t.contiguous() for t in (q, k, v))
+        yd = ctx.fused_qk_norm_rope_scatter(qd, kd, w_q, w_k, cos.to(dev), sin.to(dev), v=vd,
+                                            tags=("dq", "dk", "dv"))
+        ctx.wait()
+        torch.cuda.synchronize()
+        for a, b_, name in zip((yq, yk, yv), yd, "qkv"):
+            assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), name
 
 
 def test_c_program_uses_the_abi_alone(dev):
