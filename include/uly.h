@@ -186,8 +186,11 @@ uly_status ulysses_scatter_qkv(uly_ctx *ctx, const uly_tensor *q, const uly_tens
  * rounded once to the operand dtype (round to nearest even) and stored at
  * Y[h / Hl][b][g][h % Hl][:] — no intermediate tensor.
  * q, k: operands normalised and rotated (either may be NULL); v: optional
- *     operand scattered unchanged in the same launch, as the fused producer
- *     of [QN "Description"] stores every destination's q, k and v band.
+ *     operand scattered unchanged by the same call, as the fused producer
+ *     of [QN "Description"] stores every destination's q, k and v band: in
+ *     the same launch when the operands are interleaved (views of one fused
+ *     tensor), by the relayout kernel right after on `caller` when they are
+ *     separate dense tensors (D = 128, S_l even), where that copies faster.
  *     All members share B, S_l, D and dtype; H % P == 0 for each.
  * w_q, w_k: [D] weights in the operand dtype (required for each non-NULL
  *     q / k).  eps: > 0 (1e-6 in [QN]).
@@ -195,7 +198,7 @@ uly_status ulysses_scatter_qkv(uly_ctx *ctx, const uly_tensor *q, const uly_tens
  *     table_rows >= P*S_l.  D must be even and D*2 a multiple of 16 with
  *     D*2/16 in {4, 8, 16, 32} lanes per row (D = 32, 64, 128, 256).
  * tags / outs: as in ulysses_scatter_qkv (members 0 = q, 1 = k, 2 = v).
- * caller: the kernel runs on this stream (the compute stream). */
+ * caller: the kernels run on this stream (the compute stream). */
 uly_status fused_qk_norm_rope_scatter(uly_ctx *ctx, const uly_tensor *q, const uly_tensor *k,
                                       const uly_tensor *v, const void *w_q, const void *w_k,
                                       float eps, const float *cos_tab, const float *sin_tab,

@@ -260,9 +260,10 @@ class UlyssesContext:
 
     def fused_qk_norm_rope_scatter(self, q, k, w_q, w_k, cos, sin, eps: float = 1e-6, v=None,
                                    tags=("q", "k", "v"), out=None, stream=None):
-        """Q/K RMSNorm + interleaved RoPE + scatter in one kernel on the caller's stream.
+        """Q/K RMSNorm + interleaved RoPE + scatter, fused in one kernel, on the caller's stream.
 
-        v (optional) is scattered unchanged in the same launch.
+        v (optional) is scattered unchanged by the same call: in the same launch for
+        interleaved operands, by the relayout kernel right after for dense ones.
         cos/sin: device fp32 [rows >= P*S_l, D/2] tables indexed by global position.
         Returns the destination tensors [P, B, P*S_l, H/P, D] of (q, k, v) (None for absent members).
         """
