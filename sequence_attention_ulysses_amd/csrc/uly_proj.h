@@ -23,7 +23,10 @@ namespace uly {
 #endif
 constexpr int kProjD = 128;          // head dim the projection kernel is built for
 constexpr int kProjHeads = 2;        // heads per block, one per wave row
-constexpr int kProjTileT = 256;      // tokens per block
+#ifndef ULY_PROJ_TILE_T
+#define ULY_PROJ_TILE_T 256
+#endif
+constexpr int kProjTileT = ULY_PROJ_TILE_T;   // tokens per block
 constexpr int kProjWaveT = ULY_PROJ_WAVE_T;                            // tokens per wave
 constexpr int kProjThreads = kProjHeads * (kProjTileT / kProjWaveT) * 64;   // 8 waves (4 for 128)
 #ifndef ULY_PROJ_TILE_K

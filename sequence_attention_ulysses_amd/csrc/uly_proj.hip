@@ -70,7 +70,10 @@ constexpr int kNB = kProjD / kMf;                        // head-dim blocks per 
 constexpr int kTB = kWaveT / kMf;                        // token blocks per wave
 typedef float accv_t __attribute__((ext_vector_type(kMf * kMf / 64)));   // one block's accumulators per lane
 constexpr int kWavesT = kProjTileT / kWaveT;             // waves along the tokens
-constexpr int kWavesPerSimd = kWaves / 4;                // occupancy: one block per CU
+#ifndef ULY_PROJ_WPE
+#define ULY_PROJ_WPE (kWaves / 4)
+#endif
+constexpr int kWavesPerSimd = ULY_PROJ_WPE;              // occupancy: one block per CU by default
 static_assert(kChunks == 4 || kChunks == 8, "LDS rows of 64 or 128 bytes");
 static_assert(kWaves == kProjHeads * kWavesT && (kWaveT == 64 || kWaveT == 128), "wave grid");
 
