@@ -809,7 +809,9 @@ static uly_status fused_scatter(uly_ctx *c, const uly_tensor *q, const uly_tenso
     // bytes at the plain copy rate, faster than as band blocks (the Wan-style
     // step: 995 us against 1030 us).  In the token-tile form V rides in the
     // same launch, which reads each token's rows of all operands together.
-    const bool v_apart = band && !packed && Hrows[2] != 0;
+    // (A V of 2^31 vectors or more, beyond one relayout plan, stays in the band launch.)
+    const int64_t v_vecs = Hrows[2] ? tokens * ops[2].H * ops[2].D * ops[2].es / 16 : 0;
+    const bool v_apart = band && !packed && Hrows[2] != 0 && v_vecs < kMaxVecs;
     CopyBatch vbatch{};
     if (v_apart) {
         if ((st = plan_scatter(ops[2], c->P, dsts[2], vbatch.p[0])) != ULY_OK) return st;
