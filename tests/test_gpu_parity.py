@@ -740,7 +740,7 @@ def _random_case(rng):
     return P, B, S_l, P * Hl_q, P * Hl_k, D, dtype, pad
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(192))
 def test_random_shapes_all_paths(dev, orc, seed):
     """Random world sizes, head counts, head dims, tails, dtypes and source row
     padding through the plain scatter, the fused norm + RoPE scatter (with V) and
