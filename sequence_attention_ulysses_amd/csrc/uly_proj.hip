@@ -658,12 +658,18 @@ void proj_kernel(ProjArgs a) {
 
 }  // namespace
 
+#ifndef ULY_PROJ_DEEP_BD
+#define ULY_PROJ_DEEP_BD 3
+#endif
+static_assert(lds_slots(ULY_PROJ_DEEP_BD) * 16 <= 160 * 1024, "LDS of one workgroup");
+
 void launch_proj(const ProjArgs &a, int dtype, uint32_t blocks, bool deep_b, hipStream_t stream) {
+    constexpr int kDeep = ULY_PROJ_DEEP_BD;      // token-row ring depth for operands streaming from HBM
     if (dtype == ULY_BF16) {
-        if (deep_b) hipLaunchKernelGGL((proj_kernel<2, 3>), dim3(blocks), dim3(kProjThreads), 0, stream, a);
+        if (deep_b) hipLaunchKernelGGL((proj_kernel<2, kDeep>), dim3(blocks), dim3(kProjThreads), 0, stream, a);
         else hipLaunchKernelGGL((proj_kernel<2, 2>), dim3(blocks), dim3(kProjThreads), 0, stream, a);
     } else {
-        if (deep_b) hipLaunchKernelGGL((proj_kernel<1, 3>), dim3(blocks), dim3(kProjThreads), 0, stream, a);
+        if (deep_b) hipLaunchKernelGGL((proj_kernel<1, kDeep>), dim3(blocks), dim3(kProjThreads), 0, stream, a);
         else hipLaunchKernelGGL((proj_kernel<1, 2>), dim3(blocks), dim3(kProjThreads), 0, stream, a);
     }
 }
