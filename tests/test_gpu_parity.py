@@ -679,16 +679,32 @@ def test_two_contexts_in_flight(dev, orc):
         c2.close()
 
 
-@pytest.mark.parametrize("two_stream", [False, True])
-def test_graph_capture_replays(dev, two_stream):
+@pytest.mark.parametrize("form", ["single", "two_stream", "dense"])
+def test_graph_capture_replays(dev, form):
     """The step captured into a HIP graph: every replay, with fresh inputs written
-    eagerly between replays, matches an eager run of the same step."""
+    eagerly between replays, matches an eager run of the same step.  single: views of
+    one fused QKV tensor, V in the fused launch; two_stream: V scattered on the comm
+    stream; dense: separate Q/K/V tensors, the band kernel and then V by the relayout
+    kernel, both inside the capture."""
+    two_stream = form == "two_stream"
     P, B, S_l, H, D = 4, 1, 128, 8, 128
     qkv = synth.normal((P, B, S_l, 3, H, D), "bf16", 95, dev)
     o = synth.normal((P, B, P * S_l, H // P, D), "bf16", 96, dev)
     w_q, w_k = synth.norm_weight(D, "bf16", 97, dev), synth.norm_weight(D, "bf16", 98, dev)
     cos, sin = (t.to(dev) for t in rope_table_1d(P * S_l, D))
-    q_in, k_in, v_in = qkv[:, :, :, 0], qkv[:, :, :, 1], qkv[:, :, :, 2]
+    if form == "dense":
+        dense = [torch.empty((P, B, S_l, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+        q_in, k_in, v_in = dense
+    else:
+        q_in, k_in, v_in = qkv[:, :, :, 0], qkv[:, :, :, 1], qkv[:, :, :, 2]
+
+    def refresh(seed):
+        qkv.copy_(synth.normal(qkv.shape, "bf16", seed, dev))
+        if form == "dense":
+            for c in range(3):
+                dense[c].copy_(qkv[:, :, :, c])
+
+    refresh(95)
     ctx = UlyssesContext(P, device=0)
     try:
         def step(stream=None):
@@ -711,7 +727,7 @@ def test_graph_capture_replays(dev, two_stream):
             step(cap)
         torch.cuda.synchronize()
         for rep in range(3):
-            qkv.copy_(synth.normal(qkv.shape, "bf16", 200 + rep, dev))
+            refresh(200 + rep)
             o.copy_(synth.normal(o.shape, "bf16", 300 + rep, dev))
             torch.cuda.synchronize()
             ref = [t.clone() for t in step()]        # eager, on the current stream
