@@ -259,6 +259,24 @@ __device__ __forceinline__ Slot make_slot(const NormRopeArgs &a, uint32_t hh, ui
     const uint32_t oi = (hh_op >= a.H0 ? 1u : 0u) + (hh_op >= a.H01 ? 1u : 0u);
     const uint32_t h = hc - sel3(oi, 0u, a.H0, a.H01);
     uint32_t qd, j;
+    if constexpr (UNI) {
+        // the operand is wave-uniform: read its fields alone, from the
+        // kernel arguments at a scalar index (selecting each field among all
+        // three kept every operand's fields live and spilled 16 SGPRs)
+        const NormRopeOperand &o = a.op[oi];
+        o.hl.divmod(h, qd, j);
+        sl.s_rank = o.s_rank;
+        sl.s_b = o.s_b;
+        sl.s_s = o.s_s;
+        sl.d_b = o.d_b;
+        sl.d_g = o.d_g;
+        sl.src = o.src + int64_t(h) * o.s_h + lane * 8;
+        sl.dst = o.dst + int64_t(qd) * o.d_q + int64_t(j) * o.d_j + lane * 8;
+        sl.w = o.w + lane * 8;
+        sl.rope = oi < 2;
+        return sl;
+    }
+    // per lane: select each field among the three operands
     if (oi == 0) o0.hl.divmod(h, qd, j);
     else if (oi == 1) o1.hl.divmod(h, qd, j);
     else o2.hl.divmod(h, qd, j);
